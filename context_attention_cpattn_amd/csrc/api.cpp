@@ -1,0 +1,478 @@
+// C ABI of the context-parallel attention library: argument checks, the
+// simulated CP ring driver, the split-KV decode driver and error reporting.
+// Every check runs before the first HIP call; see include/cpattn.h for the
+// contract of each entry point.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/cpattn.h"
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+cpattn_status fail(cpattn_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+cpattn_status ok() {
+  g_err.clear();
+  return CPATTN_OK;
+}
+
+cpattn_status hip_fail(hipError_t e, const char* what) {
+  return fail(CPATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t elem_bytes(int32_t dt) { return dt == CPATTN_BF16 ? 2 : (dt == CPATTN_F32 ? 4 : 0); }
+
+int64_t numel(const cpattn_tensor& t) { return t.B * t.S * t.H * t.D; }
+
+// Shape/stride/alignment checks of one descriptor.  `lse` tensors have D == 1
+// and only need 4-byte alignment; others need 16-byte rows.
+cpattn_status check_tensor(const cpattn_tensor* t, const char* name, bool lse) {
+  if (t == nullptr) return fail(CPATTN_ERR_INVALID_ARG, "%s: descriptor is NULL", name);
+  if (t->reserved != 0) return fail(CPATTN_ERR_INVALID_ARG, "%s: reserved field must be 0", name);
+  const int64_t eb = elem_bytes(t->dtype);
+  if (eb == 0) return fail(CPATTN_ERR_INVALID_ARG, "%s: unknown dtype %d", name, (int)t->dtype);
+  if (t->B < 0 || t->S < 0 || t->H < 0 || t->D < 0)
+    return fail(CPATTN_ERR_INVALID_ARG, "%s: negative size", name);
+  if (t->stride_b < 0 || t->stride_s < 0 || t->stride_h < 0)
+    return fail(CPATTN_ERR_INVALID_ARG, "%s: negative stride", name);
+  if (lse && t->D != 1) return fail(CPATTN_ERR_INVALID_ARG, "%s: an LSE tensor must have D == 1", name);
+  if (t->B > INT32_MAX || t->S > INT32_MAX || t->H > INT32_MAX)
+    return fail(CPATTN_ERR_UNSUPPORTED, "%s: sizes beyond 2^31-1 are not supported", name);
+  if (numel(*t) == 0) return ok();
+  if (t->data == nullptr) return fail(CPATTN_ERR_INVALID_ARG, "%s: data is NULL", name);
+  const uintptr_t p = reinterpret_cast<uintptr_t>(t->data);
+  if (lse) {
+    if (p % 4) return fail(CPATTN_ERR_INVALID_ARG, "%s: data must be 4-byte aligned", name);
+  } else {
+    const int64_t q = 16 / eb;
+    if (p % 16) return fail(CPATTN_ERR_INVALID_ARG, "%s: data must be 16-byte aligned", name);
+    if (t->stride_b % q || t->stride_s % q || t->stride_h % q)
+      return fail(CPATTN_ERR_INVALID_ARG, "%s: strides must be multiples of %lld elements", name, (long long)q);
+    if (t->D > 1 && t->stride_h < t->D && t->H > 1)
+      return fail(CPATTN_ERR_INVALID_ARG, "%s: stride_h smaller than D overlaps rows", name);
+  }
+  return ok();
+}
+
+bool same_bshd(const cpattn_tensor& a, const cpattn_tensor& b) {
+  return a.B == b.B && a.S == b.S && a.H == b.H && a.D == b.D;
+}
+bool same_bsh(const cpattn_tensor& a, const cpattn_tensor& b) { return a.B == b.B && a.S == b.S && a.H == b.H; }
+bool same_strides(const cpattn_tensor& a, const cpattn_tensor& b) {
+  return a.stride_b == b.stride_b && a.stride_s == b.stride_s && a.stride_h == b.stride_h;
+}
+
+// Common checks for attention inputs q [B,Sq,Hq,D], k/v [B,Sk,Hkv,D].
+cpattn_status check_qkv(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v) {
+  cpattn_status s;
+  if ((s = check_tensor(q, "q", false)) != CPATTN_OK) return s;
+  if ((s = check_tensor(k, "k", false)) != CPATTN_OK) return s;
+  if ((s = check_tensor(v, "v", false)) != CPATTN_OK) return s;
+  if (q->dtype != k->dtype || q->dtype != v->dtype)
+    return fail(CPATTN_ERR_INVALID_ARG, "q, k and v must share one dtype");
+  if (q->B != k->B || q->B != v->B) return fail(CPATTN_ERR_INVALID_ARG, "batch sizes of q, k, v differ");
+  if (k->S != v->S || k->H != v->H) return fail(CPATTN_ERR_INVALID_ARG, "k and v shapes differ");
+  if (q->D != k->D || q->D != v->D) return fail(CPATTN_ERR_INVALID_ARG, "head_dim of q, k, v differ");
+  if (k->H < 1 || q->H < 1) return fail(CPATTN_ERR_INVALID_ARG, "head counts must be >= 1");
+  if (q->H % k->H != 0) return fail(CPATTN_ERR_INVALID_ARG, "Hq (%lld) is not a multiple of Hkv (%lld)",
+                                    (long long)q->H, (long long)k->H);
+  if (q->D != 64 && q->D != 128)
+    return fail(CPATTN_ERR_UNSUPPORTED, "head_dim %lld not supported (64 or 128)", (long long)q->D);
+  if ((int64_t)q->B * q->H > INT32_MAX / 4) return fail(CPATTN_ERR_UNSUPPORTED, "B*Hq too large");
+  return ok();
+}
+
+cpattn::PartialLaunch base_partial(const cpattn_tensor& q, const cpattn_tensor& k, const cpattn_tensor& v) {
+  cpattn::PartialLaunch a;
+  std::memset(&a, 0, sizeof a);
+  a.q = q.data;
+  a.k = k.data;
+  a.v = v.data;
+  a.q_sb = q.stride_b; a.q_ss = q.stride_s; a.q_sh = q.stride_h;
+  a.k_sb = k.stride_b; a.k_ss = k.stride_s; a.k_sh = k.stride_h;
+  a.v_sb = v.stride_b; a.v_ss = v.stride_s; a.v_sh = v.stride_h;
+  a.B = (int32_t)q.B;
+  a.Hq = (int32_t)q.H;
+  a.G = (int32_t)(q.H / k.H);
+  return a;
+}
+
+hipError_t launch_partial(const cpattn::PartialLaunch& a, int dtype, int D, int Sq, hipStream_t st) {
+  if (dtype == CPATTN_BF16) {
+    const int rpb = cpattn::partial_bf16_rows_per_block();
+    return cpattn::launch_partial_bf16(a, D, (Sq + rpb - 1) / rpb, st);
+  }
+  const int rpb = cpattn::partial_f32_rows_per_block(D);
+  return cpattn::launch_partial_f32(a, D, (Sq + rpb - 1) / rpb, st);
+}
+
+// ---- ring schedule (host side; one GPU runs every rank)
+struct Pair {
+  int q, kv;
+};
+
+// Work items of ring step s: rank r holds (Q_r, KV_{(r-s) mod P}) under
+// Pass-KV and (Q_{(r-s) mod P}, KV_r) under Pass-Q; causally empty pairs
+// (kv chunk after the q chunk) are dropped.
+std::vector<Pair> ring_step(int P, int s, int order, bool causal) {
+  std::vector<Pair> items;
+  for (int r = 0; r < P; ++r) {
+    const int other = ((r - s) % P + P) % P;
+    Pair p = (order == CPATTN_PASS_KV) ? Pair{r, other} : Pair{other, r};
+    if (causal && p.kv > p.q) continue;
+    items.push_back(p);
+  }
+  return items;
+}
+
+int64_t ring_slot(int P, int i, int j, bool causal) {
+  return causal ? (int64_t)i * (i + 1) / 2 + j : (int64_t)i * P + j;
+}
+
+int64_t ring_items(int P, bool causal) { return causal ? (int64_t)P * (P + 1) / 2 : (int64_t)P * P; }
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct RingLayout {
+  int64_t C, n_items, slot_o, slot_l;  // elements per O slot / LSE slot
+  size_t o_bytes, bytes;
+};
+
+RingLayout ring_layout(const cpattn_tensor& q, int P, bool causal) {
+  RingLayout L;
+  L.C = q.S / P;
+  L.n_items = ring_items(P, causal);
+  L.slot_o = q.B * L.C * q.H * q.D;
+  L.slot_l = q.B * L.C * q.H;
+  L.o_bytes = align_up((size_t)(L.n_items * L.slot_o) * 4);
+  L.bytes = L.o_bytes + align_up((size_t)(L.n_items * L.slot_l) * 4);
+  return L;
+}
+
+cpattn_status check_ring(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v, int n_chunks,
+                         int order, int causal) {
+  cpattn_status s;
+  if ((s = check_qkv(q, k, v)) != CPATTN_OK) return s;
+  if (k->S != q->S) return fail(CPATTN_ERR_INVALID_ARG, "ring prefill needs k/v of the same length as q");
+  if (n_chunks < 1) return fail(CPATTN_ERR_INVALID_ARG, "n_chunks must be >= 1");
+  if (n_chunks > cpattn::kMaxMerge)
+    return fail(CPATTN_ERR_UNSUPPORTED, "n_chunks above %d not supported", cpattn::kMaxMerge);
+  if (q->S % n_chunks != 0)
+    return fail(CPATTN_ERR_INVALID_ARG, "sequence length %lld not divisible by n_chunks %d", (long long)q->S, n_chunks);
+  if (order != CPATTN_PASS_KV && order != CPATTN_PASS_Q) return fail(CPATTN_ERR_INVALID_ARG, "unknown ring order");
+  if (causal != 0 && causal != 1) return fail(CPATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
+  return ok();
+}
+
+// ---- split-KV decode layout
+struct DecodeLayout {
+  int n_split, split_len, head_blocks, n_part;
+  size_t o_bytes, bytes;
+};
+
+DecodeLayout decode_layout(const cpattn_tensor& q, const cpattn_tensor& k, int n_chunks) {
+  DecodeLayout L;
+  const int64_t G = q.H / k.H;
+  L.head_blocks = (int)((G + 15) / 16);
+  const int64_t chunk = k.S / n_chunks;
+  const int64_t base_units = q.B * k.H * L.head_blocks * n_chunks;
+  int ns = 1;
+  // enough waves to keep every CU streaming, but keep splits >= 256 keys
+  while (base_units * ns < 4096 && chunk / (2 * ns) >= 256 && (int64_t)n_chunks * ns * 2 <= cpattn::kMaxMerge) ns *= 2;
+  L.n_split = ns;
+  const int64_t per = (chunk + ns - 1) / ns;
+  L.split_len = (int)((per + 31) / 32 * 32);
+  if (L.split_len == 0) L.split_len = 32;
+  L.n_part = n_chunks * ns;
+  L.o_bytes = align_up((size_t)(L.n_part * q.B * q.H * q.D) * 4);
+  L.bytes = L.o_bytes + align_up((size_t)(L.n_part * q.B * q.H) * 4);
+  return L;
+}
+
+cpattn_status check_decode(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v, int n_chunks) {
+  cpattn_status s;
+  if ((s = check_qkv(q, k, v)) != CPATTN_OK) return s;
+  if (q->dtype != CPATTN_BF16) return fail(CPATTN_ERR_UNSUPPORTED, "split-KV decode takes BF16 inputs");
+  if (q->S != 1) return fail(CPATTN_ERR_INVALID_ARG, "split-KV decode takes one query token (q.S == 1)");
+  if (n_chunks < 1) return fail(CPATTN_ERR_INVALID_ARG, "n_chunks must be >= 1");
+  if (n_chunks > cpattn::kMaxMerge)
+    return fail(CPATTN_ERR_UNSUPPORTED, "n_chunks above %d not supported", cpattn::kMaxMerge);
+  if (k->S % n_chunks != 0)
+    return fail(CPATTN_ERR_INVALID_ARG, "KV length %lld not divisible by n_chunks %d", (long long)k->S, n_chunks);
+  if (q->H / k->H > 64) return fail(CPATTN_ERR_UNSUPPORTED, "more than 64 query heads per KV head");
+  return ok();
+}
+
+cpattn_status check_out(const cpattn_tensor* out, const cpattn_tensor* lse, const cpattn_tensor& q,
+                        bool out_bf16_ok, bool lse_required) {
+  cpattn_status s;
+  if ((s = check_tensor(out, "out", false)) != CPATTN_OK) return s;
+  if (!(out->dtype == CPATTN_F32 || (out_bf16_ok && out->dtype == CPATTN_BF16)))
+    return fail(CPATTN_ERR_INVALID_ARG, "out has an unsupported dtype");
+  if (!same_bshd(*out, q)) return fail(CPATTN_ERR_INVALID_ARG, "out shape differs from q");
+  if (lse == nullptr) {
+    if (lse_required) return fail(CPATTN_ERR_INVALID_ARG, "lse descriptor is NULL");
+    return ok();
+  }
+  if ((s = check_tensor(lse, "lse", true)) != CPATTN_OK) return s;
+  if (lse->dtype != CPATTN_F32) return fail(CPATTN_ERR_INVALID_ARG, "lse must be F32");
+  if (!same_bsh(*lse, q)) return fail(CPATTN_ERR_INVALID_ARG, "lse shape differs from q's [B, S, H]");
+  return ok();
+}
+
+cpattn_status check_workspace(void* ws, size_t have, size_t need) {
+  if (need == 0) return ok();
+  if (ws == nullptr) return fail(CPATTN_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (reinterpret_cast<uintptr_t>(ws) % 16) return fail(CPATTN_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  if (have < need) return fail(CPATTN_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", have, need);
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* cpattn_last_error(void) { return g_err.c_str(); }
+
+const char* cpattn_version(void) { return "cpattn 0.1.0 gfx950"; }
+
+cpattn_status cpattn_partial(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                             int64_t q_offset, int64_t kv_offset, int causal, cpattn_tensor* out,
+                             cpattn_tensor* lse, void* stream) {
+  cpattn_status s;
+  if ((s = check_qkv(q, k, v)) != CPATTN_OK) return s;
+  if ((s = check_out(out, lse, *q, false, true)) != CPATTN_OK) return s;
+  if (q_offset < 0 || kv_offset < 0) return fail(CPATTN_ERR_INVALID_ARG, "offsets must be >= 0");
+  if (causal != 0 && causal != 1) return fail(CPATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (q->S == 0 || q->B == 0) return ok();
+
+  cpattn::PartialLaunch a = base_partial(*q, *k, *v);
+  a.o = static_cast<float*>(out->data);
+  a.lse = static_cast<float*>(lse->data);
+  a.o_sb = out->stride_b; a.o_ss = out->stride_s; a.o_sh = out->stride_h;
+  a.l_sb = lse->stride_b; a.l_ss = lse->stride_s; a.l_sh = lse->stride_h;
+  a.q_pos0 = q_offset;
+  a.kv_pos0 = kv_offset;
+  a.chunk_len = 0;
+  a.Sq = (int32_t)q->S;
+  a.Sk = (int32_t)k->S;
+  a.causal = causal;
+  a.n_items = 1;
+  a.items[0] = cpattn::Item{0, 0, 0};
+  const hipError_t e = launch_partial(a, q->dtype, (int)q->D, (int)q->S, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "partial attention launch");
+  return ok();
+}
+
+cpattn_status cpattn_merge(const cpattn_tensor* partials, const cpattn_tensor* lses, int n, cpattn_tensor* out,
+                           cpattn_tensor* out_lse, void* stream) {
+  if (partials == nullptr || lses == nullptr) return fail(CPATTN_ERR_INVALID_ARG, "partials/lses array is NULL");
+  if (n < 1 || n > cpattn::kMaxMerge) return fail(CPATTN_ERR_INVALID_ARG, "n must be in [1, %d]", cpattn::kMaxMerge);
+  cpattn_status s;
+  const cpattn_tensor& p0 = partials[0];
+  const cpattn_tensor& l0 = lses[0];
+  for (int c = 0; c < n; ++c) {
+    if ((s = check_tensor(&partials[c], "partial", false)) != CPATTN_OK) return s;
+    if ((s = check_tensor(&lses[c], "partial lse", true)) != CPATTN_OK) return s;
+    if (partials[c].dtype != CPATTN_F32 || lses[c].dtype != CPATTN_F32)
+      return fail(CPATTN_ERR_INVALID_ARG, "partials and their LSE must be F32");
+    if (!same_bshd(partials[c], p0) || !same_strides(partials[c], p0))
+      return fail(CPATTN_ERR_INVALID_ARG, "partial %d differs in shape or strides from partial 0", c);
+    if (!same_bsh(lses[c], p0) || !same_strides(lses[c], l0))
+      return fail(CPATTN_ERR_INVALID_ARG, "lse %d differs in shape or strides", c);
+  }
+  if (p0.D != 64 && p0.D != 128)
+    return fail(CPATTN_ERR_UNSUPPORTED, "head_dim %lld not supported (64 or 128)", (long long)p0.D);
+  if ((s = check_out(out, out_lse, p0, true, false)) != CPATTN_OK) return s;
+  if (numel(p0) == 0) return ok();
+
+  cpattn::MergeLaunch m;
+  std::memset(&m, 0, sizeof m);
+  for (int c = 0; c < n; ++c) {
+    m.o[c] = static_cast<const float*>(partials[c].data);
+    m.lse[c] = static_cast<const float*>(lses[c].data);
+  }
+  m.n = n;
+  m.out_bf16 = out->dtype == CPATTN_BF16;
+  m.B = (int32_t)p0.B; m.S = (int32_t)p0.S; m.H = (int32_t)p0.H; m.D = (int32_t)p0.D;
+  m.p_sb = p0.stride_b; m.p_ss = p0.stride_s; m.p_sh = p0.stride_h;
+  m.pl_sb = l0.stride_b; m.pl_ss = l0.stride_s; m.pl_sh = l0.stride_h;
+  m.out = out->data;
+  m.o_sb = out->stride_b; m.o_ss = out->stride_s; m.o_sh = out->stride_h;
+  if (out_lse != nullptr) {
+    m.out_lse = static_cast<float*>(out_lse->data);
+    m.ol_sb = out_lse->stride_b; m.ol_ss = out_lse->stride_s; m.ol_sh = out_lse->stride_h;
+  }
+  const hipError_t e = cpattn::launch_merge(m, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return ok();
+}
+
+size_t cpattn_ring_prefill_workspace_size(const cpattn_tensor* q, int n_chunks, cpattn_order order, int causal) {
+  if (check_tensor(q, "q", false) != CPATTN_OK) return 0;
+  if (n_chunks < 1 || q->S % n_chunks != 0) {
+    fail(CPATTN_ERR_INVALID_ARG, "n_chunks must be >= 1 and divide the sequence length");
+    return 0;
+  }
+  if (order != CPATTN_PASS_KV && order != CPATTN_PASS_Q) {
+    fail(CPATTN_ERR_INVALID_ARG, "unknown ring order");
+    return 0;
+  }
+  ok();
+  return ring_layout(*q, n_chunks, causal != 0).bytes;
+}
+
+cpattn_status cpattn_ring_prefill(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                                  int n_chunks, cpattn_order order, int causal, cpattn_tensor* out,
+                                  cpattn_tensor* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  cpattn_status s;
+  if ((s = check_ring(q, k, v, n_chunks, order, causal)) != CPATTN_OK) return s;
+  if ((s = check_out(out, lse, *q, true, false)) != CPATTN_OK) return s;
+  const bool cz = causal != 0;
+  const RingLayout L = ring_layout(*q, n_chunks, cz);
+  if (q->S == 0 || q->B == 0) return ok();
+  if ((s = check_workspace(workspace, workspace_bytes, L.bytes)) != CPATTN_OK) return s;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int P = n_chunks;
+  float* ws_o = static_cast<float*>(workspace);
+  float* ws_l = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.o_bytes);
+
+  // partials, one launch per ring step (all ranks of the step together)
+  cpattn::PartialLaunch a = base_partial(*q, *k, *v);
+  a.o = ws_o;
+  a.lse = ws_l;
+  a.o_sh = q->D; a.o_ss = q->H * q->D; a.o_sb = L.C * q->H * q->D;
+  a.l_sh = 1; a.l_ss = q->H; a.l_sb = L.C * q->H;
+  a.o_slot = L.slot_o;
+  a.l_slot = L.slot_l;
+  a.q_pos0 = 0;
+  a.kv_pos0 = 0;
+  a.chunk_len = L.C;
+  a.Sq = (int32_t)L.C;
+  a.Sk = (int32_t)L.C;
+  a.causal = causal;
+  std::vector<std::vector<int>> arrivals(P);
+  for (int step = 0; step < P; ++step) {
+    const std::vector<Pair> items = ring_step(P, step, order, cz);
+    a.n_items = 0;
+    for (const Pair& p : items) {
+      a.items[a.n_items++] = cpattn::Item{p.q, p.kv, (int32_t)ring_slot(P, p.q, p.kv, cz)};
+      arrivals[p.q].push_back(p.kv);
+    }
+    if (a.n_items == 0) continue;
+    const hipError_t e = launch_partial(a, q->dtype, (int)q->D, (int)L.C, st);
+    if (e != hipSuccess) return hip_fail(e, "ring step launch");
+  }
+
+  // each owner merges its partials in arrival order
+  for (int i = 0; i < P; ++i) {
+    cpattn::MergeLaunch m;
+    std::memset(&m, 0, sizeof m);
+    m.n = (int32_t)arrivals[i].size();
+    for (int c = 0; c < m.n; ++c) {
+      const int64_t slot = ring_slot(P, i, arrivals[i][c], cz);
+      m.o[c] = ws_o + slot * L.slot_o;
+      m.lse[c] = ws_l + slot * L.slot_l;
+    }
+    m.out_bf16 = out->dtype == CPATTN_BF16;
+    m.B = (int32_t)q->B; m.S = (int32_t)L.C; m.H = (int32_t)q->H; m.D = (int32_t)q->D;
+    m.p_sb = a.o_sb; m.p_ss = a.o_ss; m.p_sh = a.o_sh;
+    m.pl_sb = a.l_sb; m.pl_ss = a.l_ss; m.pl_sh = a.l_sh;
+    m.out = static_cast<char*>(out->data) + (size_t)(i * L.C * out->stride_s) * elem_bytes(out->dtype);
+    m.o_sb = out->stride_b; m.o_ss = out->stride_s; m.o_sh = out->stride_h;
+    if (lse != nullptr) {
+      m.out_lse = static_cast<float*>(lse->data) + i * L.C * lse->stride_s;
+      m.ol_sb = lse->stride_b; m.ol_ss = lse->stride_s; m.ol_sh = lse->stride_h;
+    }
+    const hipError_t e = cpattn::launch_merge(m, st);
+    if (e != hipSuccess) return hip_fail(e, "ring merge launch");
+  }
+  return ok();
+}
+
+size_t cpattn_splitkv_decode_workspace_size(const cpattn_tensor* q, const cpattn_tensor* k, int n_chunks) {
+  if (check_tensor(q, "q", false) != CPATTN_OK || check_tensor(k, "k", false) != CPATTN_OK) return 0;
+  if (k->H < 1 || q->H % k->H != 0) {
+    fail(CPATTN_ERR_INVALID_ARG, "Hq must be a positive multiple of Hkv");
+    return 0;
+  }
+  if (n_chunks < 1 || n_chunks > cpattn::kMaxMerge || k->S % n_chunks != 0) {
+    fail(CPATTN_ERR_INVALID_ARG, "n_chunks must be in [1, %d] and divide the KV length", cpattn::kMaxMerge);
+    return 0;
+  }
+  ok();
+  return decode_layout(*q, *k, n_chunks).bytes;
+}
+
+cpattn_status cpattn_splitkv_decode(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                                    int n_chunks, cpattn_tensor* out, cpattn_tensor* lse, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  cpattn_status s;
+  if ((s = check_decode(q, k, v, n_chunks)) != CPATTN_OK) return s;
+  if ((s = check_out(out, lse, *q, true, false)) != CPATTN_OK) return s;
+  if (q->B == 0) return ok();
+  const DecodeLayout L = decode_layout(*q, *k, n_chunks);
+  if ((s = check_workspace(workspace, workspace_bytes, L.bytes)) != CPATTN_OK) return s;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float* ws_o = static_cast<float*>(workspace);
+  float* ws_l = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.o_bytes);
+
+  cpattn::DecodeLaunch d;
+  std::memset(&d, 0, sizeof d);
+  d.q = q->data; d.k = k->data; d.v = v->data;
+  d.o = ws_o; d.lse = ws_l;
+  d.q_sb = q->stride_b; d.q_sh = q->stride_h;
+  d.k_sb = k->stride_b; d.k_ss = k->stride_s; d.k_sh = k->stride_h;
+  d.v_sb = v->stride_b; d.v_ss = v->stride_s; d.v_sh = v->stride_h;
+  d.B = (int32_t)q->B; d.Hq = (int32_t)q->H; d.Hkv = (int32_t)k->H; d.G = (int32_t)(q->H / k->H);
+  d.Skv = (int32_t)k->S;
+  d.n_chunks = n_chunks;
+  d.n_split = L.n_split;
+  d.split_len = L.split_len;
+  d.head_blocks = L.head_blocks;
+  hipError_t e = cpattn::launch_decode_bf16(d, (int)q->D, st);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+
+  cpattn::MergeLaunch m;
+  std::memset(&m, 0, sizeof m);
+  m.n = L.n_part;
+  const int64_t part_o = q->B * q->H * q->D, part_l = q->B * q->H;
+  for (int c = 0; c < m.n; ++c) {
+    m.o[c] = ws_o + c * part_o;
+    m.lse[c] = ws_l + c * part_l;
+  }
+  m.out_bf16 = out->dtype == CPATTN_BF16;
+  m.B = (int32_t)q->B; m.S = 1; m.H = (int32_t)q->H; m.D = (int32_t)q->D;
+  m.p_sb = q->H * q->D; m.p_ss = q->H * q->D; m.p_sh = q->D;
+  m.pl_sb = q->H; m.pl_ss = q->H; m.pl_sh = 1;
+  m.out = out->data;
+  m.o_sb = out->stride_b; m.o_ss = out->stride_s; m.o_sh = out->stride_h;
+  if (lse != nullptr) {
+    m.out_lse = static_cast<float*>(lse->data);
+    m.ol_sb = lse->stride_b; m.ol_ss = lse->stride_s; m.ol_sh = lse->stride_h;
+  }
+  e = cpattn::launch_merge(m, st);
+  if (e != hipSuccess) return hip_fail(e, "decode merge launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,79 @@
+// Device helpers shared by the gfx950 kernels: vector types, MFMA wrappers,
+// base-2 transcendentals and the XCD-aware workgroup order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cpattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// Hardware base-2 exponential and logarithm (v_exp_f32 / v_log_f32).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// D(32x32) += A(32x16) * B(16x32), bf16 inputs, fp32 accumulate.
+// Lane l supplies A row (l % 32), k-slots 8*(l/32) .. +7, and B column
+// (l % 32) for the same k-slots; it receives D[8*(i/4) + 4*(l/32) + i%4][l % 32]
+// in element i of the accumulator.
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// D(16x16) += A(16x32) * B(32x16).  Lane l supplies A row (l % 16), k-slots
+// 8*(l/16) .. +7, B column (l % 16) for the same k-slots, and receives
+// D[4*(l/16) + i][l % 16] in element i.
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& x) { return __builtin_bit_cast(bf16x8, x); }
+__device__ __forceinline__ u32x4 as_u32x4(const bf16x8& x) { return __builtin_bit_cast(u32x4, x); }
+
+// Two floats to packed bf16 (round to nearest even), low half = a.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  bf16x2 v = __builtin_convertvector((f32x2){a, b}, bf16x2);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Byte-select of two dwords: v_perm_b32.
+__device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+// {lo16(a), lo16(b)} and {hi16(a), hi16(b)}
+__device__ __forceinline__ uint32_t pack_lo16(uint32_t a, uint32_t b) { return perm_b32(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) { return perm_b32(b, a, 0x07060302u); }
+
+__device__ __forceinline__ u32x4 ld_global16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ u32x4 ld_lds16(const uint8_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ u32x2 ld_lds8(const uint8_t* p) { return *reinterpret_cast<const u32x2*>(p); }
+__device__ __forceinline__ void st_lds16(uint8_t* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ void st_lds8(uint8_t* p, const u32x2& v) { *reinterpret_cast<u32x2*>(p) = v; }
+
+// Value of the lane 32 positions away (lanes 0..31 <-> 32..63).
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup w runs on
+// XCD w % 8).  Give each XCD a contiguous range of logical tiles so tiles that
+// share K/V (adjacent heads of one query tile) share that XCD's L2.
+__device__ __forceinline__ int xcd_logical_block(int w, int total) {
+  const int per = total >> 3;
+  const int full = per << 3;
+  return (w < full) ? ((w & 7) * per + (w >> 3)) : w;
+}
+
+}  // namespace cpattn

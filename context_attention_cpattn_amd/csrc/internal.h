@@ -1,0 +1,80 @@
+// Internal launch interface between the C ABI (api.cpp) and the HIP kernels.
+// Not installed; the public interface is include/cpattn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cpattn {
+
+constexpr int kMaxItems = 64;   // partial-attention work items per launch
+constexpr int kMaxMerge = 64;   // partials per merge launch (CPATTN_MAX_MERGE)
+
+// One (Q block, K/V block) pair of a launch.  Pointers are derived from the
+// launch's base pointers: Q rows start at q_chunk * chunk_len, K/V rows at
+// kv_chunk * chunk_len, and the outputs go to slot `slot` of the output base.
+struct Item {
+  int32_t q_chunk;
+  int32_t kv_chunk;
+  int32_t slot;
+};
+
+struct PartialLaunch {
+  const void* q;  // element type: bf16 or float, per the launcher
+  const void* k;
+  const void* v;
+  float* o;
+  float* lse;
+  int64_t q_sb, q_ss, q_sh;  // element strides
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int64_t l_sb, l_ss, l_sh;
+  int64_t o_slot, l_slot;    // element distance between output slots
+  int64_t q_pos0, kv_pos0;   // global position of row 0 of chunk 0
+  int64_t chunk_len;         // rows per chunk (used only to derive item pointers)
+  int32_t B, Sq, Sk, Hq, G;  // Sq/Sk: rows of one Q/K/V block; G = Hq / Hkv
+  int32_t causal;
+  int32_t n_items;
+  Item items[kMaxItems];
+};
+
+struct MergeLaunch {
+  const float* o[kMaxMerge];
+  const float* lse[kMaxMerge];
+  int32_t n;
+  int32_t out_bf16;
+  int32_t B, S, H, D;
+  int64_t p_sb, p_ss, p_sh;   // partial O strides (shared)
+  int64_t pl_sb, pl_ss, pl_sh;  // partial LSE strides (shared)
+  void* out;
+  int64_t o_sb, o_ss, o_sh;
+  float* out_lse;             // may be null
+  int64_t ol_sb, ol_ss, ol_sh;
+};
+
+struct DecodeLaunch {
+  const void* q;  // bf16 [B, 1, Hq, D]
+  const void* k;  // bf16 [B, Skv, Hkv, D]
+  const void* v;
+  float* o;       // workspace partials: [n_part][B][Hq][D]
+  float* lse;     // workspace LSE:      [n_part][B][Hq]
+  int64_t q_sb, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int32_t B, Hq, Hkv, G, Skv;
+  int32_t n_chunks, n_split;  // partial p = chunk * n_split + split
+  int32_t split_len;          // keys per split (multiple of 32, last split may be shorter)
+  int32_t head_blocks;        // ceil(G / 16)
+};
+
+// Launchers return hipSuccess or the launch error.
+hipError_t launch_partial_bf16(const PartialLaunch& a, int D, int n_qtiles, hipStream_t s);
+hipError_t launch_partial_f32(const PartialLaunch& a, int D, int n_qtiles, hipStream_t s);
+hipError_t launch_merge(const MergeLaunch& a, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeLaunch& a, int D, hipStream_t s);
+
+int partial_bf16_rows_per_block();  // query rows per workgroup of the bf16 kernel
+int partial_f32_rows_per_block(int D);
+
+}  // namespace cpattn

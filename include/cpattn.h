@@ -1,0 +1,189 @@
+/*
+ * cpattn.h - C ABI of the MI355X (gfx950) context-parallel attention library.
+ *
+ * The library computes exact causal softmax attention over a sequence that is
+ * partitioned into context-parallel (CP) chunks, the way the CP section of
+ * "Scaling LLM Inference: Innovations in Tensor Parallelism, Context
+ * Parallelism, and Expert Parallelism" describes it (techreport.ngo rewrite,
+ * section "Context Parallelism for Million-Token Contexts"): the sequence is
+ * divided among the CP ranks, every rank produces Q, K and V for its own
+ * tokens, and then either its K/V (Pass-KV) or its Q (Pass-Q) moves from rank
+ * to rank until each query has met the whole context.  The reader notes on
+ * the same article (soumitrasaha.com, "The communication bottleneck across
+ * all three axes") add that the K/V pieces circulate on a ring and the
+ * per-step results are combined into the full-context output.  One GPU plays
+ * every rank in turn; the ring exchange becomes a choice of chunk pointers.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Tensors are described by cpattn_tensor: a device pointer plus sizes and
+ *    element strides of a [B, S, H, D] view whose last (D) axis is contiguous.
+ *    Q/K/V/O use that layout; an LSE tensor uses it with D = 1 ([B, S, H]).
+ *  - Scores are scaled by 1/sqrt(D).  Query head h reads KV head
+ *    h / (Hq / Hkv) (grouped-query attention; Hq must be a multiple of Hkv).
+ *  - Causal visibility: key row j of a K/V block whose first row sits at
+ *    global position kv_offset is visible to query row i of a Q block whose
+ *    first row sits at q_offset iff kv_offset + j <= q_offset + i (the
+ *    diagonal is visible).
+ *  - LSE is the natural log of the sum of exp(scaled score) over visible keys.
+ *    A row that sees no key gets LSE = -inf and an all-zero output row.
+ *  - Supported: D in {64, 128}; Q/K/V all BF16 (bf16 MFMA, fp32 accumulate)
+ *    or all F32 (fp32 vector arithmetic).  Partial outputs and LSE are F32.
+ *  - Alignment: every data pointer 16-byte aligned; for Q/K/V/O the strides
+ *    (stride_b, stride_s, stride_h) are multiples of 16 bytes' worth of
+ *    elements (8 for BF16, 4 for F32).  LSE strides are unconstrained.
+ *  - Ownership: the caller owns every buffer and the stream.  The library
+ *    allocates no device memory and keeps no pointer after a call returns;
+ *    the drivers use only the caller's workspace.  Outputs must not alias
+ *    inputs or each other.
+ *  - Errors: all argument checks run before any HIP call.  On a non-OK
+ *    status nothing has been enqueued or written and cpattn_last_error()
+ *    (thread-local) describes the problem.  CPATTN_OK means the work is
+ *    enqueued on `stream` (a hipStream_t; NULL is the default stream);
+ *    execution errors surface at the caller's next synchronisation.
+ *  - Results are deterministic: no atomics on any accumulation path, and a
+ *    fixed reduction order, so repeated calls give bitwise-identical output.
+ */
+#ifndef CPATTN_H
+#define CPATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CPATTN_MAX_MERGE 64   /* most partials one cpattn_merge call accepts */
+
+typedef enum cpattn_status {
+  CPATTN_OK = 0,
+  CPATTN_ERR_INVALID_ARG = 1,   /* null pointer, shape/stride/alignment mismatch, bad count */
+  CPATTN_ERR_UNSUPPORTED = 2,   /* valid request outside what the kernels implement (e.g. D) */
+  CPATTN_ERR_WORKSPACE = 3,     /* workspace missing or smaller than the size query returned */
+  CPATTN_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+} cpattn_status;
+
+typedef enum cpattn_dtype { CPATTN_BF16 = 0, CPATTN_F32 = 1 } cpattn_dtype;
+
+typedef enum cpattn_order { CPATTN_PASS_KV = 0, CPATTN_PASS_Q = 1 } cpattn_order;
+
+typedef struct cpattn_tensor {
+  void* data;        /* device pointer (may be NULL only when the tensor is empty) */
+  int32_t dtype;     /* cpattn_dtype */
+  int32_t reserved;  /* must be 0 */
+  int64_t B, S, H, D;                   /* sizes; D = 1 for LSE tensors */
+  int64_t stride_b, stride_s, stride_h; /* element strides; the D axis has stride 1 */
+} cpattn_tensor;
+
+/*
+ * cpattn_partial - attention of one local Q block against one K/V block.
+ *
+ * The unit of work of one ring step: a rank's local queries against the K/V
+ * chunk it holds at that step (techreport.ngo rewrite, "Context Parallelism
+ * for Million-Token Contexts", Pass-KV and Pass-Q bullets).
+ *   q   [B, Sq, Hq, D]   BF16 or F32, rows at global positions q_offset + i
+ *   k,v [B, Sk, Hkv, D]  same dtype as q, rows at kv_offset + j
+ *   out [B, Sq, Hq, D]   F32: softmax(scale * q k^T, masked) v, normalised by
+ *                        this block's own denominator
+ *   lse [B, Sq, Hq]      F32 (D = 1): natural-log LSE of this block's scores
+ * q_offset, kv_offset >= 0; causal is 0 or 1.  Rows that see no key of this
+ * block (possible under the causal mask) get out = 0 and lse = -inf.
+ */
+cpattn_status cpattn_partial(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                             int64_t q_offset, int64_t kv_offset, int causal,
+                             cpattn_tensor* out, cpattn_tensor* lse, void* stream);
+
+/*
+ * cpattn_merge - combine n partial (O, LSE) results of the same rows.
+ *
+ * The step that turns the pieces gathered around the ring into the
+ * full-context result (soumitrasaha.com reader notes, "The communication
+ * bottleneck across all three axes"), done by the exact log-sum-exp rule:
+ *   M = max_c lse_c,  w_c = exp(lse_c - M),
+ *   out = sum_c w_c O_c / sum_c w_c,  out_lse = M + ln(sum_c w_c);
+ * rows whose partials all have lse = -inf give out = 0, out_lse = -inf.
+ *   partials[c] [B, S, H, D] F32, c = 0..n-1, all with the same sizes and
+ *               strides (host array of n descriptors)
+ *   lses[c]     [B, S, H] F32, all with the same strides
+ *   out         [B, S, H, D] F32 or BF16 (rounded to nearest even)
+ *   out_lse     [B, S, H] F32, or NULL to skip
+ * 1 <= n <= CPATTN_MAX_MERGE.  Sums run in the array order, so the result is
+ * bitwise reproducible for a given order (any order is correct up to
+ * rounding).
+ */
+cpattn_status cpattn_merge(const cpattn_tensor* partials, const cpattn_tensor* lses, int n,
+                           cpattn_tensor* out, cpattn_tensor* out_lse, void* stream);
+
+/*
+ * cpattn_ring_prefill_workspace_size - bytes of workspace cpattn_ring_prefill
+ * needs for this q, chunk count, order and mask (0 if the arguments are
+ * invalid; cpattn_last_error() then says why).
+ */
+size_t cpattn_ring_prefill_workspace_size(const cpattn_tensor* q, int n_chunks, cpattn_order order,
+                                          int causal);
+
+/*
+ * cpattn_ring_prefill - full-sequence attention by a simulated CP ring.
+ *
+ * The sequence of q/k/v is cut into n_chunks equal contiguous chunks, chunk
+ * c holding tokens [c*C, (c+1)*C) and owned by rank c.  Ring step s gives
+ * rank r the pair (Q chunk r, K/V chunk (r - s) mod P) under CPATTN_PASS_KV,
+ * or (Q chunk (r - s) mod P, K/V chunk r) under CPATTN_PASS_Q (techreport.ngo
+ * rewrite, "Context Parallelism for Million-Token Contexts": the two variants
+ * differ only in whether K/V or Q moves between ranks).  Under the causal mask, pairs whose
+ * K/V chunk lies after the Q chunk see nothing and are skipped.  All ranks'
+ * partials of one step run in one launch; each Q chunk's partials are then
+ * merged in the order they reached its owner (Pass-KV: own chunk first, then
+ * the earlier chunks in ring order; Pass-Q: own chunk first, then chunks
+ * 0, 1, ...).
+ *   q   [B, S, Hq, D], k/v [B, S, Hkv, D]  (same S), BF16 or F32
+ *   out [B, S, Hq, D]  F32 or BF16
+ *   lse [B, S, Hq]     F32, or NULL
+ *   workspace          device buffer of at least
+ *                      cpattn_ring_prefill_workspace_size(q, n_chunks, order, causal) bytes
+ * n_chunks >= 1 must divide S.
+ */
+cpattn_status cpattn_ring_prefill(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                                  int n_chunks, cpattn_order order, int causal,
+                                  cpattn_tensor* out, cpattn_tensor* lse,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * cpattn_splitkv_decode_workspace_size - bytes of workspace
+ * cpattn_splitkv_decode needs (0 if the arguments are invalid).
+ */
+size_t cpattn_splitkv_decode_workspace_size(const cpattn_tensor* q, const cpattn_tensor* k, int n_chunks);
+
+/*
+ * cpattn_splitkv_decode - one new token per sequence against a cached K/V
+ * that is split into n_chunks equal chunks.
+ *
+ * Decode reads the KV cache and is memory-bandwidth bound (techreport.ngo
+ * rewrite, "Why Parallelism Defines LLM Serving Cost"; reader notes, "The
+ * communication bottleneck across all three axes"); the cache grows
+ * linearly with context ("Context Parallelism for Million-Token Contexts").
+ * Each chunk (further cut into sub-splits chosen by the library) yields a
+ * partial (O, LSE) that is merged into the result.  The new token sits at
+ * position Skv - 1 and sees every cached key.
+ *   q   [B, 1, Hq, D]    BF16
+ *   k,v [B, Skv, Hkv, D] BF16
+ *   out [B, 1, Hq, D]    F32 or BF16
+ *   lse [B, 1, Hq]       F32, or NULL
+ * n_chunks >= 1 must divide Skv; Hq / Hkv <= 64.
+ */
+cpattn_status cpattn_splitkv_decode(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                                    int n_chunks, cpattn_tensor* out, cpattn_tensor* lse,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* cpattn_last_error(void);
+
+/* Library version string, e.g. "cpattn 0.1.0 gfx950". */
+const char* cpattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CPATTN_H */

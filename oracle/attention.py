@@ -8,12 +8,13 @@ What it computes is the plain definition of exact softmax attention, written
 out in float64 with torch CPU primitives (matmul, max, exp, log, sum).  The
 pages (Meta's "Scaling LLM Inference: Innovations in Tensor Parallelism,
 Context Parallelism, and Expert Parallelism", and the reader notes on it) fix
-only the structure: the sequence is split across CP ranks, each rank computes
-its local Q, K and V, and either K/V (Pass-KV) or Q (Pass-Q) travels around a
-ring so that every query sees the full context ("Context Parallelism for
-Million-Token Contexts"; the reader notes' section "The communication
-bottleneck across all three axes": K/V pass around a ring to accumulate the
-full attention result).  Where the pages are silent this oracle takes the
+only the structure: the sequence is divided among CP ranks, every rank
+produces Q, K and V for its own tokens, and either its K/V (Pass-KV) or its Q
+(Pass-Q) moves from rank to rank until each query has met the whole context
+("Context Parallelism for Million-Token Contexts"; the reader notes' section
+"The communication bottleneck across all three axes" adds that the K/V
+pieces circulate on a ring and the per-step results combine into the
+full-context output).  Where the pages are silent this oracle takes the
 plainest reading:
 
 * causal mask with the diagonal included: key position ``kv_offset + j`` is
@@ -72,27 +73,27 @@ def partial_attention(q, k, v, q_offset: int = 0, kv_offset: int = 0, causal: bo
     if Sq == 0 or Sk == 0:
         return out, lse
     for b in range(B):
-        for h in range(Hq):
-            g = h // G
+        for g in range(Hkv):
             kk = k[b, :, g, :].to(F64)  # [Sk, D]
             vv = v[b, :, g, :].to(F64)
-            for r0 in range(0, Sq, row_block):
-                r1 = min(Sq, r0 + row_block)
-                qq = q[b, r0:r1, h, :].to(F64)  # [R, D]
-                s = alpha * (qq @ kk.T)  # scaled scores [R, Sk]
-                vis = visible_mask(r1 - r0, Sk, q_offset + r0, kv_offset, causal)
-                s = s.masked_fill(~vis, NEG_INF)
-                m = s.max(dim=1, keepdim=True).values  # -inf for rows that see nothing
-                has = torch.isfinite(m).squeeze(1)
-                m_safe = torch.where(torch.isfinite(m), m, torch.zeros_like(m))
-                l = torch.exp(s - m_safe).sum(dim=1, keepdim=True)
-                row_lse = m_safe + torch.log(l)  # log of zero -> -inf for empty rows
-                p = torch.exp(s - torch.where(has.unsqueeze(1), row_lse, torch.zeros_like(row_lse)))
-                o = p @ vv
-                o[~has] = 0.0
-                row_lse[~has] = NEG_INF
-                out[b, r0:r1, h, :] = o
-                lse[b, r0:r1, h] = row_lse.squeeze(1)
+            for h in range(g * G, (g + 1) * G):  # the query heads that read KV head g
+                for r0 in range(0, Sq, row_block):
+                    r1 = min(Sq, r0 + row_block)
+                    qq = q[b, r0:r1, h, :].to(F64)  # [R, D]
+                    s = alpha * (qq @ kk.T)  # scaled scores [R, Sk]
+                    vis = visible_mask(r1 - r0, Sk, q_offset + r0, kv_offset, causal)
+                    s = s.masked_fill(~vis, NEG_INF)
+                    m = s.max(dim=1, keepdim=True).values  # -inf for rows that see nothing
+                    has = torch.isfinite(m).squeeze(1)
+                    m_safe = torch.where(torch.isfinite(m), m, torch.zeros_like(m))
+                    l = torch.exp(s - m_safe).sum(dim=1, keepdim=True)
+                    row_lse = m_safe + torch.log(l)  # log of zero -> -inf for empty rows
+                    p = torch.exp(s - torch.where(has.unsqueeze(1), row_lse, torch.zeros_like(row_lse)))
+                    o = p @ vv
+                    o[~has] = 0.0
+                    row_lse[~has] = NEG_INF
+                    out[b, r0:r1, h, :] = o
+                    lse[b, r0:r1, h] = row_lse.squeeze(1)
     return out, lse
 
 
@@ -109,6 +110,8 @@ def attention_rows(q_rows, k, v, positions, causal: bool = True):
     ``0..positions[r]`` (causal) or all keys.  Returns (O [B,R,Hq,D], lse [B,R,Hq]).
     """
     B, R, Hq, D = q_rows.shape
+    k = k.to(F64)  # convert the long K/V once, not once per row
+    v = v.to(F64)
     out = torch.zeros(B, R, Hq, D, dtype=F64)
     lse = torch.full((B, R, Hq), NEG_INF, dtype=F64)
     for r, pos in enumerate(list(int(p) for p in positions)):

@@ -1,0 +1,195 @@
+"""C ABI checks that need no GPU: the library loads, exports what the header
+declares, and every argument check fails before any HIP call.
+
+Only invalid calls are made here (plus zero-size no-ops), so no kernel is
+ever launched; the fake device pointers are never dereferenced.  On a machine
+with a visible GPU these tests are skipped, since a validation bug there could
+turn a fake pointer into a real launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cpattn.h")
+
+cp = pytest.importorskip("context_attention_cpattn_amd")
+T = cp.Tensor
+lib = cp.lib
+
+no_gpu = pytest.mark.skipif(torch.cuda.is_available(), reason="validation probes use fake device pointers")
+
+FAKE = 0x100000  # 16-byte aligned, never dereferenced
+
+
+def header_symbols():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\w[\w\s\*]*?\b(cpattn_\w+)\s*\(", txt, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    syms = header_symbols()
+    assert {"cpattn_partial", "cpattn_merge", "cpattn_ring_prefill", "cpattn_ring_prefill_workspace_size",
+            "cpattn_splitkv_decode", "cpattn_splitkv_decode_workspace_size", "cpattn_last_error",
+            "cpattn_version"} <= set(syms)
+    raw = ctypes.CDLL(cp.LIB_PATH)
+    for s in syms:
+        assert hasattr(raw, s), f"{s} declared in cpattn.h but not exported"
+
+
+def test_version():
+    v = cp.version()
+    assert v.startswith("cpattn ") and "gfx950" in v
+
+
+def bshd(B, S, H, D, dt=cp.DT_BF16, ptr=FAKE):
+    return T(ptr, dt, 0, B, S, H, D, S * H * D, H * D, D)
+
+
+def lse_of(B, S, H, ptr=FAKE):
+    return T(ptr, cp.DT_F32, 0, B, S, H, 1, S * H, H, 1)
+
+
+def call_partial(q, k, v, out, lse, qo=0, ko=0, causal=1):
+    r = ctypes.byref
+    return lib.cpattn_partial(r(q) if q else None, r(k), r(v), qo, ko, causal, r(out), r(lse) if lse else None, None)
+
+
+def err():
+    return lib.cpattn_last_error().decode()
+
+
+@no_gpu
+def test_partial_validation():
+    q, k, v = bshd(1, 64, 4, 128), bshd(1, 64, 2, 128), bshd(1, 64, 2, 128)
+    out, lse = bshd(1, 64, 4, 128, cp.DT_F32), lse_of(1, 64, 4)
+    assert call_partial(None, k, v, out, lse) == cp.ERR_INVALID_ARG and "NULL" in err()
+    assert call_partial(q, k, v, out, None) == cp.ERR_INVALID_ARG
+    # dtype mismatch
+    assert call_partial(q, bshd(1, 64, 2, 128, cp.DT_F32), v, out, lse) == cp.ERR_INVALID_ARG
+    # unsupported head dim
+    assert call_partial(bshd(1, 64, 4, 96), bshd(1, 64, 2, 96), bshd(1, 64, 2, 96),
+                        bshd(1, 64, 4, 96, cp.DT_F32), lse) == cp.ERR_UNSUPPORTED
+    # Hq not a multiple of Hkv
+    assert call_partial(bshd(1, 64, 3, 128), k, v, bshd(1, 64, 3, 128, cp.DT_F32),
+                        lse_of(1, 64, 3)) == cp.ERR_INVALID_ARG and "multiple" in err()
+    # misaligned pointer and stride
+    assert call_partial(bshd(1, 64, 4, 128, ptr=FAKE + 8), k, v, out, lse) == cp.ERR_INVALID_ARG
+    bad = bshd(1, 64, 4, 128)
+    bad.stride_s = 4 * 128 + 4
+    assert call_partial(bad, k, v, out, lse) == cp.ERR_INVALID_ARG and "multiples" in err()
+    # partial output must be F32, lse must be [B,S,H] with D == 1
+    assert call_partial(q, k, v, bshd(1, 64, 4, 128, cp.DT_BF16), lse) == cp.ERR_INVALID_ARG
+    bad_lse = lse_of(1, 64, 4)
+    bad_lse.D = 2
+    assert call_partial(q, k, v, out, bad_lse) == cp.ERR_INVALID_ARG
+    assert call_partial(q, k, v, out, lse_of(1, 63, 4)) == cp.ERR_INVALID_ARG
+    # offsets, mask flag, reserved field, unknown dtype, negative size
+    assert call_partial(q, k, v, out, lse, qo=-1) == cp.ERR_INVALID_ARG
+    assert call_partial(q, k, v, out, lse, causal=2) == cp.ERR_INVALID_ARG
+    r = bshd(1, 64, 4, 128)
+    r.reserved = 1
+    assert call_partial(r, k, v, out, lse) == cp.ERR_INVALID_ARG
+    assert call_partial(bshd(1, 64, 4, 128, dt=7), k, v, out, lse) == cp.ERR_INVALID_ARG
+    assert call_partial(bshd(1, -1, 4, 128), k, v, out, lse) == cp.ERR_INVALID_ARG
+    # batch mismatch, k/v mismatch
+    assert call_partial(q, bshd(2, 64, 2, 128), v, out, lse) == cp.ERR_INVALID_ARG
+    assert call_partial(q, k, bshd(1, 65, 2, 128), out, lse) == cp.ERR_INVALID_ARG
+
+
+@no_gpu
+def test_partial_empty_is_a_noop():
+    q = bshd(1, 0, 4, 128, ptr=None)
+    out = bshd(1, 0, 4, 128, cp.DT_F32, ptr=None)
+    lse = lse_of(1, 0, 4, ptr=None)
+    assert call_partial(q, bshd(1, 64, 2, 128), bshd(1, 64, 2, 128), out, lse) == cp.OK
+
+
+@no_gpu
+def test_merge_validation():
+    r = ctypes.byref
+    P = (T * 2)(bshd(1, 8, 2, 64, cp.DT_F32), bshd(1, 8, 2, 64, cp.DT_F32))
+    L = (T * 2)(lse_of(1, 8, 2), lse_of(1, 8, 2))
+    out = bshd(1, 8, 2, 64, cp.DT_F32)
+    assert lib.cpattn_merge(P, L, 0, r(out), None, None) == cp.ERR_INVALID_ARG
+    assert lib.cpattn_merge(P, L, cp.MAX_MERGE + 1, r(out), None, None) == cp.ERR_INVALID_ARG
+    assert lib.cpattn_merge(None, L, 2, r(out), None, None) == cp.ERR_INVALID_ARG
+    P2 = (T * 2)(bshd(1, 8, 2, 64, cp.DT_F32), bshd(1, 9, 2, 64, cp.DT_F32))
+    assert lib.cpattn_merge(P2, L, 2, r(out), None, None) == cp.ERR_INVALID_ARG and "partial 1" in err()
+    P3 = (T * 2)(bshd(1, 8, 2, 64, cp.DT_F32), bshd(1, 8, 2, 64, cp.DT_BF16))
+    assert lib.cpattn_merge(P3, L, 2, r(out), None, None) == cp.ERR_INVALID_ARG
+    assert lib.cpattn_merge(P, L, 2, r(bshd(1, 8, 2, 128, cp.DT_F32)), None, None) == cp.ERR_INVALID_ARG
+    P4 = (T * 1)(bshd(1, 8, 2, 32, cp.DT_F32))
+    assert lib.cpattn_merge(P4, L, 1, r(bshd(1, 8, 2, 32, cp.DT_F32)), None, None) == cp.ERR_UNSUPPORTED
+
+
+def ring_ws(q, n, order=0, causal=1):
+    return lib.cpattn_ring_prefill_workspace_size(ctypes.byref(q), n, order, causal)
+
+
+def test_ring_workspace_size_formula():
+    # 128K-token shape, 16 chunks: 136 causal items, each fp32 O [1, 8192, 16, 128] and LSE [1, 8192, 16]
+    q = bshd(1, 131072, 16, 128)
+    n_items = 16 * 17 // 2
+    o = n_items * 8192 * 16 * 128 * 4
+    l = n_items * 8192 * 16 * 4
+    up = lambda x: (x + 255) // 256 * 256
+    assert ring_ws(q, 16) == up(o) + up(l)
+    assert ring_ws(q, 16, causal=0) == up(256 * 8192 * 16 * 128 * 4) + up(256 * 8192 * 16 * 4)
+    assert ring_ws(q, 16, order=1) == ring_ws(q, 16, order=0)
+    assert ring_ws(q, 3) == 0 and "divide" in err()
+    assert ring_ws(q, 0) == 0
+    assert ring_ws(q, 16, order=5) == 0
+
+
+@no_gpu
+def test_ring_validation():
+    r = ctypes.byref
+    q, k, v = bshd(1, 512, 4, 64), bshd(1, 512, 1, 64), bshd(1, 512, 1, 64)
+    out, lse = bshd(1, 512, 4, 64, cp.DT_F32), lse_of(1, 512, 4)
+    need = ring_ws(q, 4)
+    assert need > 0
+
+    def call(n=4, order=0, causal=1, ws=FAKE, nbytes=None, k_=k, out_=out):
+        return lib.cpattn_ring_prefill(r(q), r(k_), r(v), n, order, causal, r(out_), r(lse), ws,
+                                       need if nbytes is None else nbytes, None)
+
+    assert call(n=3) == cp.ERR_INVALID_ARG
+    assert call(n=0) == cp.ERR_INVALID_ARG
+    assert call(n=128) == cp.ERR_UNSUPPORTED
+    assert call(order=9) == cp.ERR_INVALID_ARG
+    assert call(causal=-1) == cp.ERR_INVALID_ARG
+    assert call(ws=None) == cp.ERR_WORKSPACE
+    assert call(nbytes=need - 1) == cp.ERR_WORKSPACE and "needed" in err()
+    assert call(ws=FAKE + 4) == cp.ERR_WORKSPACE
+    assert call(k_=bshd(1, 256, 1, 64)) == cp.ERR_INVALID_ARG
+    assert call(out_=bshd(1, 512, 4, 64, dt=7)) == cp.ERR_INVALID_ARG
+
+
+@no_gpu
+def test_decode_validation():
+    r = ctypes.byref
+    q, k, v = bshd(4, 1, 16, 128), bshd(4, 4096, 1, 128), bshd(4, 4096, 1, 128)
+    out = bshd(4, 1, 16, 128, cp.DT_F32)
+    need = lib.cpattn_splitkv_decode_workspace_size(r(q), r(k), 8)
+    assert need > 0
+
+    def call(q_=q, k_=k, v_=v, n=8, nbytes=need, ws=FAKE):
+        return lib.cpattn_splitkv_decode(r(q_), r(k_), r(v_), n, r(out), None, ws, nbytes, None)
+
+    assert call(q_=bshd(4, 2, 16, 128)) == cp.ERR_INVALID_ARG
+    f32 = lambda t: T(t.data, cp.DT_F32, 0, t.B, t.S, t.H, t.D, t.stride_b, t.stride_s, t.stride_h)
+    assert call(q_=f32(q), k_=f32(k), v_=f32(v)) == cp.ERR_UNSUPPORTED
+    assert call(n=3) == cp.ERR_INVALID_ARG
+    assert call(nbytes=need - 16) == cp.ERR_WORKSPACE
+    assert call(q_=bshd(4, 1, 128, 128)) in (cp.ERR_INVALID_ARG, cp.ERR_UNSUPPORTED)
+    assert lib.cpattn_splitkv_decode_workspace_size(r(q), r(k), 3) == 0
+
+
+def test_last_error_cleared_by_success():
+    q = bshd(1, 512, 4, 64)
+    assert ring_ws(q, 3) == 0 and err() != ""
+    assert ring_ws(q, 4) > 0 and err() == ""

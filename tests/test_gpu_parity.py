@@ -1,0 +1,218 @@
+"""GPU parity: the HIP path against the fp64 oracle on the same seeded inputs.
+
+Every call goes through the C ABI (via the ctypes binding).  Inputs come from
+``seeded_inputs``; expected values come from ``oracle`` only.
+"""
+import math
+
+import pytest
+import torch
+
+import oracle
+import seeded_inputs as si
+from gpu_util import BF16_TOL, F32_TOL, banner, compare
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def cp():
+    import context_attention_cpattn_amd as m
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    return m
+
+
+def draw(seed, shape, dtype, tensor_id=0):
+    return si.draw_tensor(seed, tensor_id, shape, dtype)
+
+
+# (B, Sq, Sk, Hq, Hkv, D, q_offset, kv_offset, causal)
+PARTIAL_CASES = [
+    (1, 256, 256, 2, 1, 128, 0, 0, True),        # diagonal block, 2 query tiles
+    (1, 300, 300, 2, 1, 128, 1000, 1000, True),  # diagonal, ragged (300 = 2*128 + 44)
+    (2, 128, 512, 4, 2, 128, 512, 0, True),      # K/V block entirely in the past
+    (1, 200, 77, 3, 1, 128, 0, 500, True),       # K/V block entirely in the future: all masked
+    (1, 257, 333, 2, 2, 128, 100, 37, True),     # odd offsets straddling the diagonal
+    (1, 130, 190, 4, 1, 128, 0, 0, False),       # no mask, ragged both ways
+    (1, 256, 256, 2, 1, 64, 0, 0, True),         # D = 64
+    (2, 190, 300, 4, 4, 64, 150, 0, True),       # D = 64, GQA off, ragged
+    (1, 1, 1000, 16, 1, 128, 999, 0, True),      # one query row (decode-like shape)
+    (1, 64, 0, 2, 1, 128, 0, 0, True),           # empty K/V block
+]
+
+
+@pytest.mark.parametrize("case", PARTIAL_CASES, ids=lambda c: "B{}_Sq{}_Sk{}_H{}-{}_D{}_off{}-{}_c{}".format(*c))
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_partial_matches_oracle(cp, case, dtype):
+    B, Sq, Sk, Hq, Hkv, D, qo, ko, causal = case
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    seed = 1000 + Sq + 7 * Sk + D
+    q = draw(seed, (B, Sq, Hq, D), tdt, 0)
+    k = draw(seed, (B, Sk, Hkv, D), tdt, 1)
+    v = draw(seed, (B, Sk, Hkv, D), tdt, 2)
+    o_ref, l_ref = oracle.partial_attention(q, k, v, qo, ko, causal)
+    banner("partial", dtype, case)
+    o, l = cp.partial(q.to(DEV), k.to(DEV), v.to(DEV), qo, ko, causal)
+    torch.cuda.synchronize()
+    compare(o, l, o_ref, l_ref, BF16_TOL if dtype == "bf16" else F32_TOL, f"partial {dtype} {case}")
+
+
+def test_partial_strided_views(cp):
+    """Non-contiguous views (head-sliced, padded rows) through the descriptor strides."""
+    B, S, H, D = 2, 200, 6, 128
+    big_q = draw(77, (B, S, H + 2, D), torch.bfloat16, 0)
+    big_k = draw(77, (B, S, 3, D), torch.bfloat16, 1)
+    big_v = draw(77, (B, S, 3, D), torch.bfloat16, 2)
+    q, k, v = big_q[:, :, 1:H + 1], big_k[:, :, 1:3], big_v[:, :, 1:3]
+    o_ref, l_ref = oracle.partial_attention(q, k, v, 10, 0, True)
+    gq, gk, gv = big_q.to(DEV)[:, :, 1:H + 1], big_k.to(DEV)[:, :, 1:3], big_v.to(DEV)[:, :, 1:3]
+    out_big = torch.full((B, S, H + 1, D), float("nan"), device=DEV)
+    lse_big = torch.full((B, S, H + 3), float("nan"), device=DEV)
+    banner("partial strided")
+    o, l = cp.partial(gq, gk, gv, 10, 0, True, out=out_big[:, :, :H], lse=lse_big[:, :, 2:2 + H])
+    torch.cuda.synchronize()
+    compare(o, l, o_ref, l_ref, BF16_TOL, "partial strided")
+    assert torch.isnan(out_big[:, :, H]).all() and torch.isnan(lse_big[:, :, :2]).all()
+    assert torch.isnan(lse_big[:, :, 2 + H:]).all()
+
+
+@pytest.mark.parametrize("n", [1, 2, 5, 64])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_merge_matches_oracle(cp, n, out_dtype):
+    B, S, H, D = 2, 37, 3, 128
+    parts = [draw(500 + c, (B, S, H, D), torch.float32, 0) for c in range(n)]
+    lses = [4.0 * draw(500 + c, (B, S, H), torch.float32, 1) for c in range(n)]
+    if n > 1:  # some partials with nothing visible, and one row where every partial is empty
+        lses[1][0, :5] = float("-inf")
+        for c in range(n):
+            lses[c][1, 3, 2] = float("-inf")
+    o_ref, l_ref = oracle.merge(parts, lses)
+    banner("merge", n, out_dtype)
+    o, l = cp.merge([p.to(DEV) for p in parts], [x.to(DEV) for x in lses], out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    tol = F32_TOL if out_dtype == torch.float32 else BF16_TOL
+    compare(o.float(), l, o_ref, l_ref, tol, f"merge n={n} {out_dtype}")
+
+
+def test_merge_bf16_rounding_is_nearest_even(cp):
+    p = draw(9, (1, 16, 2, 64), torch.float32, 0)
+    lse = torch.zeros(1, 16, 2)
+    o, _ = cp.merge([p.to(DEV)], [lse.to(DEV)], out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o.cpu(), p.to(torch.bfloat16))
+
+
+# ----------------------------------------------------------------------------
+# The five workloads
+# ----------------------------------------------------------------------------
+
+def test_workload_tiny_f32_unchunked(cp):
+    w = si.WORKLOADS["tiny_f32_s512_p4"]
+    q, k, v = si.make_qkv(w)
+    o_ref, l_ref = oracle.full_attention(q, k, v, causal=True)  # unchunked reference
+    banner(w.name, "pass_kv", w.n_chunks)
+    o, l = cp.ring_prefill(q.to(DEV), k.to(DEV), v.to(DEV), w.n_chunks, "pass_kv", True)
+    torch.cuda.synchronize()
+    compare(o, l, o_ref, l_ref, BF16_TOL, w.name + " (workload tolerance)")
+    compare(o, l, o_ref, l_ref, F32_TOL, w.name + " (fp32 tolerance)")
+
+
+def test_workload_tiny_bf16_copy(cp):
+    w = si.WORKLOADS["tiny_f32_s512_p4"]
+    q, k, v = si.make_qkv(w, torch.bfloat16)
+    o_ref, l_ref = oracle.ring_attention(q, k, v, w.n_chunks, oracle.PASS_KV, True)
+    for order in ("pass_kv", "pass_q"):
+        banner(w.name, "bf16", order)
+        o, l = cp.ring_prefill(q.to(DEV), k.to(DEV), v.to(DEV), w.n_chunks, order, True)
+        torch.cuda.synchronize()
+        compare(o, l, o_ref, l_ref, BF16_TOL, f"{w.name} bf16 {order}")
+
+
+@pytest.mark.parametrize("P,order,causal", [(1, "pass_kv", True), (3, "pass_q", True), (5, "pass_kv", False),
+                                            (6, "pass_q", False), (8, "pass_kv", True)])
+def test_ring_small_orders(cp, P, order, causal):
+    S = 120 * P  # 120-token chunks: one ragged query tile per chunk
+    q = draw(31 + P, (1, S, 4, 128), torch.bfloat16, 0)
+    k = draw(31 + P, (1, S, 2, 128), torch.bfloat16, 1)
+    v = draw(31 + P, (1, S, 2, 128), torch.bfloat16, 2)
+    o_ref, l_ref = oracle.full_attention(q, k, v, causal)
+    banner("ring", P, order, causal)
+    o, l = cp.ring_prefill(q.to(DEV), k.to(DEV), v.to(DEV), P, order, causal, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    compare(o, l, o_ref, l_ref, BF16_TOL, f"ring P={P} {order} causal={causal}")
+    o16, _ = cp.ring_prefill(q.to(DEV), k.to(DEV), v.to(DEV), P, order, causal, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o16.cpu(), o.cpu().to(torch.bfloat16))
+
+
+def test_workload_gqa_8k(cp):
+    w = si.WORKLOADS["gqa16_bf16_s8k_p8"]
+    q, k, v = si.make_qkv(w)
+    banner(w.name, "oracle")
+    o_ref, l_ref = oracle.full_attention(q, k, v, causal=True)
+    banner(w.name, "pass_kv", w.n_chunks)
+    o, l = cp.ring_prefill(q.to(DEV), k.to(DEV), v.to(DEV), w.n_chunks, "pass_kv", True)
+    torch.cuda.synchronize()
+    compare(o, l, o_ref, l_ref, BF16_TOL, w.name)
+
+
+def test_workload_decode_32k(cp):
+    w = si.WORKLOADS["decode_b128_kv32k_p8"]
+    q, k, v = si.make_qkv(w)
+    banner(w.name, "oracle")
+    o_ref, l_ref = oracle.splitkv_decode(q, k, v, w.n_chunks)
+    gq, gk, gv = q.to(DEV), k.to(DEV), v.to(DEV)
+    banner(w.name, "splitkv_decode", w.n_chunks)
+    o, l = cp.splitkv_decode(gq, gk, gv, w.n_chunks)
+    torch.cuda.synchronize()
+    compare(o, l, o_ref, l_ref, BF16_TOL, w.name)
+    # the same result through the generic entry points: 8 partials, then a merge
+    C = w.chunk
+    parts = [cp.partial(gq, gk[:, c * C:(c + 1) * C], gv[:, c * C:(c + 1) * C], w.Skv - 1, c * C, True)
+             for c in range(w.n_chunks)]
+    o2, l2 = cp.merge([p[0] for p in parts], [p[1] for p in parts])
+    torch.cuda.synchronize()
+    compare(o2, l2, o_ref, l_ref, BF16_TOL, w.name + " via partial+merge")
+
+
+def _sampled_check(cp, w, o, l, q, k, v, name):
+    rows = si.sampled_rows(w, 64)
+    o_ref, l_ref = oracle.attention_rows(q[:, rows], k, v, rows, causal=True)
+    idx = torch.as_tensor(rows, device=o.device)
+    compare(o.index_select(1, idx), l.index_select(1, idx), o_ref, l_ref, BF16_TOL, name + " (64 sampled rows)")
+
+
+def test_workload_128k_both_orders(cp):
+    w = si.WORKLOADS["prefill_bf16_s128k_p16"]
+    q, k, v = si.make_qkv(w)
+    gq, gk, gv = q.to(DEV), k.to(DEV), v.to(DEV)
+    res = {}
+    for order in w.orders:
+        banner(w.name, order, w.n_chunks)
+        res[order] = cp.ring_prefill(gq, gk, gv, w.n_chunks, order, True)
+        torch.cuda.synchronize()
+        _sampled_check(cp, w, *res[order], q, k, v, f"{w.name} {order}")
+    (okv, lkv), (oq, lq) = res["pass_kv"], res["pass_q"]
+    d_o = (okv - oq).abs().max().item()
+    d_l = (lkv - lq).abs().max().item()
+    print(f"[parity] {w.name}: pass_kv vs pass_q max|dO|={d_o:.3e} max|dLSE|={d_l:.3e}", flush=True)
+    assert d_o <= 1e-5 and d_l <= 1e-5
+    # properties over every row: finite output, LSE within its possible range
+    assert torch.isfinite(okv).all() and torch.isfinite(lkv).all()
+
+
+@pytest.mark.timeout(900)
+def test_workload_1m_sampled(cp):
+    w = si.WORKLOADS["prefill_bf16_s1m_p8"]
+    banner(w.name, "drawing inputs")
+    q, k, v = si.make_qkv(w)
+    gq, gk, gv = q.to(DEV), k.to(DEV), v.to(DEV)
+    banner(w.name, "pass_kv", w.n_chunks)
+    o, l = cp.ring_prefill(gq, gk, gv, w.n_chunks, "pass_kv", True)
+    torch.cuda.synchronize()
+    banner(w.name, "oracle on sampled rows")
+    _sampled_check(cp, w, o, l, q, k, v, w.name)
+    del o, l, gq, gk, gv
+    torch.cuda.empty_cache()

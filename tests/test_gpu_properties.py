@@ -1,0 +1,138 @@
+"""GPU properties that hold at any size: determinism, closed forms, causality,
+guard bands, and the decode shape checked against its own definition."""
+import math
+
+import pytest
+import torch
+
+import oracle
+import seeded_inputs as si
+from gpu_util import BF16_TOL, banner, compare
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def cp():
+    import context_attention_cpattn_amd as m
+    assert torch.cuda.is_available()
+    return m
+
+
+def qkv(seed, S, Hq, Hkv, D, dtype=torch.bfloat16, B=1):
+    return (si.draw_tensor(seed, 0, (B, S, Hq, D), dtype).to(DEV),
+            si.draw_tensor(seed, 1, (B, S, Hkv, D), dtype).to(DEV),
+            si.draw_tensor(seed, 2, (B, S, Hkv, D), dtype).to(DEV))
+
+
+def test_bitwise_deterministic(cp):
+    q, k, v = qkv(3, 2048, 8, 1, 128)
+    banner("determinism ring")
+    a = cp.ring_prefill(q, k, v, 4, "pass_kv", True)
+    b = cp.ring_prefill(q, k, v, 4, "pass_kv", True)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    qd = si.draw_tensor(4, 0, (8, 1, 16, 128), torch.bfloat16).to(DEV)
+    kd = si.draw_tensor(4, 1, (8, 8192, 1, 128), torch.bfloat16).to(DEV)
+    vd = si.draw_tensor(4, 2, (8, 8192, 1, 128), torch.bfloat16).to(DEV)
+    banner("determinism decode")
+    a = cp.splitkv_decode(qd, kd, vd, 4)
+    b = cp.splitkv_decode(qd, kd, vd, 4)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_zero_query_closed_form(cp):
+    """Q = 0: every visible score is 0, so LSE = ln(#visible) and O is the prefix mean of V."""
+    S = 1000
+    _, k, v = qkv(5, S, 2, 1, 128)
+    q = torch.zeros(1, S, 2, 128, dtype=torch.bfloat16, device=DEV)
+    banner("zero query")
+    o, l = cp.ring_prefill(q, k, v, 4, "pass_kv", True)
+    torch.cuda.synchronize()
+    cnt = torch.arange(1, S + 1, dtype=torch.float64)
+    assert (l.double().cpu()[0, :, 0] - cnt.log()).abs().max() < 1e-5
+    prefix_mean = v.double().cpu()[0, :, 0].cumsum(0) / cnt.unsqueeze(1)
+    assert (o.double().cpu()[0, :, 1] - prefix_mean).abs().max() < 1e-5
+
+
+def test_constant_v_gives_constant_o(cp):
+    q, k, _ = qkv(6, 1536, 4, 1, 128)
+    v = torch.full((1, 1536, 1, 128), 0.75, dtype=torch.bfloat16, device=DEV)
+    banner("constant V")
+    o, _ = cp.ring_prefill(q, k, v, 3, "pass_q", True)
+    torch.cuda.synchronize()
+    assert (o - 0.75).abs().max().item() < 2e-3  # only bf16 rounding of P is left
+
+
+def test_causality_future_perturbation(cp):
+    q, k, v = qkv(7, 1024, 4, 1, 128)
+    banner("causality")
+    o1, l1 = cp.ring_prefill(q, k, v, 4, "pass_kv", True)
+    cut = 517
+    k2, v2 = k.clone(), v.clone()
+    k2[:, cut + 1:] = -k2[:, cut + 1:] * 3
+    v2[:, cut + 1:] = v2[:, cut + 1:] + 5
+    o2, l2 = cp.ring_prefill(q, k2, v2, 4, "pass_kv", True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[:, :cut + 1], o2[:, :cut + 1]) and torch.equal(l1[:, :cut + 1], l2[:, :cut + 1])
+    assert not torch.equal(o1[:, cut + 1:], o2[:, cut + 1:])
+
+
+def test_output_guard_bands(cp):
+    """Outputs written through views inside NaN-filled buffers touch only their own elements."""
+    B, S, H, D = 1, 640, 4, 128
+    q, k, v = qkv(8, S, H, 1, D)
+    big = torch.full((B, S + 64, H, D), float("nan"), device=DEV)
+    big_l = torch.full((B, S + 64, H), float("nan"), device=DEV)
+    banner("guard bands")
+    cp.ring_prefill(q, k, v, 5, "pass_kv", True, out=big[:, 32:32 + S], lse=big_l[:, 32:32 + S])
+    torch.cuda.synchronize()
+    assert torch.isnan(big[:, :32]).all() and torch.isnan(big[:, 32 + S:]).all()
+    assert torch.isnan(big_l[:, :32]).all() and torch.isnan(big_l[:, 32 + S:]).all()
+    assert torch.isfinite(big[:, 32:32 + S]).all() and torch.isfinite(big_l[:, 32:32 + S]).all()
+
+
+def test_peaked_rows(cp):
+    """A query that matches one key much better than the rest returns (almost exactly) that key's V."""
+    S, D = 256, 128
+    k = torch.zeros(1, S, 1, D)
+    for j in range(S):
+        k[0, j, 0, j % D] = 1.0 if j < D else -1.0
+    v = si.draw_tensor(9, 2, (1, S, 1, D), torch.float32)
+    q = torch.zeros(1, S, 1, D)
+    for i in range(S):
+        q[0, i, 0, min(i, D - 1) % D] = 64.0  # scaled score 64/sqrt(128) ~ 5.7 above the rest
+    qb, kb, vb = q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+    o_ref, l_ref = oracle.full_attention(qb, kb, vb, True)
+    banner("peaked")
+    o, l = cp.ring_prefill(qb.to(DEV), kb.to(DEV), vb.to(DEV), 2, "pass_kv", True)
+    torch.cuda.synchronize()
+    compare(o, l, o_ref, l_ref, BF16_TOL, "peaked rows")
+
+
+def test_decode_lse_of_zero_query(cp):
+    B, Skv = 4, 4096
+    q = torch.zeros(B, 1, 16, 128, dtype=torch.bfloat16, device=DEV)
+    k = si.draw_tensor(10, 1, (B, Skv, 1, 128), torch.bfloat16).to(DEV)
+    v = si.draw_tensor(10, 2, (B, Skv, 1, 128), torch.bfloat16).to(DEV)
+    banner("decode zero query")
+    o, l = cp.splitkv_decode(q, k, v, 8)
+    torch.cuda.synchronize()
+    assert (l.double() - math.log(Skv)).abs().max().item() < 1e-5
+    mean = v.double().mean(dim=1, keepdim=True).expand(B, 1, 16, 128)
+    assert (o.double() - mean).abs().max().item() < 1e-5
+
+
+@pytest.mark.parametrize("B,Skv,G,Hkv,n", [(3, 1000, 16, 1, 4), (2, 4096, 8, 2, 8), (1, 2048, 40, 1, 2),
+                                            (5, 96, 16, 1, 3), (2, 8192, 16, 1, 1)])
+def test_decode_shapes(cp, B, Skv, G, Hkv, n):
+    q = si.draw_tensor(11, 0, (B, 1, G * Hkv, 128), torch.bfloat16)
+    k = si.draw_tensor(11, 1, (B, Skv, Hkv, 128), torch.bfloat16)
+    v = si.draw_tensor(11, 2, (B, Skv, Hkv, 128), torch.bfloat16)
+    o_ref, l_ref = oracle.splitkv_decode(q, k, v, n)
+    banner("decode", B, Skv, G, Hkv, n)
+    o, l = cp.splitkv_decode(q.to(DEV), k.to(DEV), v.to(DEV), n)
+    torch.cuda.synchronize()
+    compare(o, l, o_ref, l_ref, BF16_TOL, f"decode B{B} Skv{Skv} G{G} Hkv{Hkv} n{n}")
