@@ -1,0 +1,338 @@
+#!/usr/bin/env python3
+"""Benchmark of the context-parallel causal attention hot path on one MI355X.
+
+Headline (``value``): causal prefill attention TFLOP/s (unmasked FLOPs only:
+4 * D * Hq per visible (query, key) pair) on the 128K-token workload --
+1 x 131072 tokens, 16 query heads on 1 KV head, head_dim 128, bf16, seed 3,
+cut into 16 CP chunks of 8192 and run in Pass-KV ring order.  One step is one
+full pass: the 16 ring-step launches (all simulated ranks of a step in one
+launch) and the per-owner log-sum-exp merges.  Inputs are resident in HBM
+before timing starts.
+
+The same JSON line also carries the dominant kernel's roofline (partial
+attention, measured with HIP events around each ring-step launch on the
+stream the library launches on), the split-KV decode leg (GB/s on the
+128 x 32768-key decode workload), the Pass-Q ordering of the prefill, the
+merge kernel's bandwidth, and the fp64 CPU oracle timed on a bounded sample.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1]
+  python bench.py --summarize-pmc FETCH_DIR WRITE_DIR   # traffic summary from two rocprofv3 --pmc runs
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import csv
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 4096 bf16 FLOP/clk x 2.4 GHz (dense)
+PEAK_HBM_GBS = 8000.0       # HBM3E
+METRIC = "causal prefill attention TFLOP/s & % bf16 MFMA peak; decode GB/s & % HBM peak"
+PREFILL = "prefill_bf16_s128k_p16"
+DECODE = "decode_b128_kv32k_p8"
+KERNEL_SRC = os.path.join(ROOT, "context_attention_cpattn_amd", "csrc", "partial_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "partial_bf16_prefill_s128k_p16_traffic.txt")
+COPY_BYTES = 1 << 30
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("partial_bf16.hip", "device.h", "internal.h"):
+        with open(os.path.join(ROOT, "context_attention_cpattn_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def ring_step_flops(w, order: str):
+    """Unmasked FLOPs of each ring step: 4*D*Hq*B per visible (query, key) pair."""
+    P, C = w.n_chunks, w.chunk
+    per_pair = 4.0 * w.D * w.Hq * w.B
+    out = []
+    for s in range(P):
+        f = 0.0
+        for r in range(P):
+            other = (r - s) % P
+            qi, kj = (r, other) if order == "pass_kv" else (other, r)
+            if w.causal and kj > qi:
+                continue
+            f += per_pair * (C * (C + 1) / 2 if (w.causal and kj == qi) else C * C)
+        out.append(f)
+    return out
+
+
+def read_traffic():
+    """Per-launch HBM traffic of the partial kernel from the committed pmc summary, if current."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for ln in open(TRAFFIC_FILE):
+        if ":" in ln and not ln.startswith("#"):
+            a, b = ln.split(":", 1)
+            kv[a.strip()] = b.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, q, k, v, seconds: float):
+    """fp64 oracle on sampled full-context rows of the prefill workload, on the host cores."""
+    import torch
+
+    import oracle
+    import seeded_inputs as si
+
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    torch.set_num_threads(threads)
+    rows = si.sampled_rows(w, 1024)
+    rng = __import__("random").Random(0)
+    rows = rows[rng.sample(range(len(rows)), len(rows))]
+    k64, v64 = k.to(torch.float64), v.to(torch.float64)
+    done_flops, n = 0.0, 0
+    t0 = time.perf_counter()
+    for pos in rows:
+        pos = int(pos)
+        oracle.attention_rows(q[:, pos:pos + 1], k64[:, :pos + 1], v64[:, :pos + 1], [pos], causal=True)
+        done_flops += 4.0 * w.D * w.Hq * w.B * (pos + 1)
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": f"{n} query rows x {w.Hq} heads of {w.name} at full causal context (fp64, torch CPU), "
+                      f"{done_flops:.3e} FLOP in {dt:.1f} s"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--order", default="pass_kv", choices=["pass_kv", "pass_q"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB fp32 copy kernel (counter calibration under rocprofv3 --pmc)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    args = ap.parse_args(argv)
+
+    if args.summarize_pmc:
+        return summarize_pmc(*args.summarize_pmc)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
+              "the simulated CP ranks all run on one device.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import context_attention_cpattn_amd as cp
+    import seeded_inputs as si
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    w = si.WORKLOADS[PREFILL]
+    log(f"[bench] {props.name}, {cp.version()}; drawing {w.name} inputs")
+    q, k, v = si.make_qkv(w)
+    gq, gk, gv = q.to(dev), k.to(dev), v.to(dev)
+    P = w.n_chunks
+    ws = torch.empty(cp.ring_prefill_workspace_size(gq, P, args.order, True), dtype=torch.uint8, device=dev)
+    out = torch.empty(w.q_shape(), dtype=torch.float32, device=dev)
+    lse = torch.empty(w.q_shape()[:3], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    step_flops = ring_step_flops(w, args.order)
+    total_flops = w.flops()
+    assert abs(sum(step_flops) - total_flops) / total_flops < 1e-9
+
+    def one_step(ev=None):
+        for s in range(P):
+            if ev is not None:
+                ev[s][0].record(stream)
+            cp.ring_step(gq, gk, gv, P, s, ws, args.order, True)
+            if ev is not None:
+                ev[s][1].record(stream)
+        if ev is not None:
+            ev[P][0].record(stream)
+        cp.ring_merge(P, ws, out, lse, args.order, True)
+        if ev is not None:
+            ev[P][1].record(stream)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(P + 1)]
+              for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+    value = total_flops / (wall / args.steps) / 1e12
+
+    # dominant kernel: the partial-attention launches (one per ring step)
+    k_ms = [[events[i][s][0].elapsed_time(events[i][s][1]) for s in range(P)] for i in range(args.steps)]
+    m_ms = [events[i][P][0].elapsed_time(events[i][P][1]) for i in range(args.steps)]
+    kern_ms_total = sum(sum(x) for x in k_ms)
+    launches = args.steps * P
+    avg_launch_ms = kern_ms_total / launches
+    achieved = total_flops * args.steps / (kern_ms_total * 1e-3) / 1e12
+    traffic = read_traffic()
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "kernel": "partial_bf16_kernel<128>", "launches_per_step": P,
+                "avg_launch_ms": round(avg_launch_ms, 4),
+                "algorithmic_flop_per_launch": total_flops / P}
+    per_step_tflops = [round(step_flops[s] / (sum(k_ms[i][s] for i in range(args.steps)) / args.steps * 1e-3) / 1e12, 1)
+                       for s in range(P)]
+    # merge bandwidth: every owner reads its partials (O fp32 + LSE) and writes O fp32 + LSE
+    C, row_bytes = w.chunk, 4 * (w.D + 1)
+    n_parts = sum(i + 1 for i in range(P))
+    merge_bytes = (n_parts + P) * C * w.Hq * w.B * row_bytes
+    merge_ms = sum(m_ms) / len(m_ms)
+    log(f"[bench] step {ms_per_step:.2f} ms, {value:.1f} TFLOP/s; partial kernel {achieved:.1f} TFLOP/s; "
+        f"merge {merge_ms:.3f} ms")
+
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "order": args.order, "B": w.B, "S": w.Sq, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "D": w.D, "n_chunks": P, "causal": True, "seed": w.seed, "inputs": "N(0,1) rounded to bf16",
+                   "flop_per_step": total_flops},
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": roofline,
+        "per_ring_step_tflops": per_step_tflops,
+        "merge": {"ms_per_step": round(merge_ms, 4), "GB/s": round(merge_bytes / (merge_ms * 1e-3) / 1e9, 1),
+                  "frac_hbm": round(merge_bytes / (merge_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                  "algorithmic_bytes": merge_bytes},
+        "device": props.name,
+    }
+
+    # Pass-Q ordering of the same prefill (a few steps)
+    other = "pass_q" if args.order == "pass_kv" else "pass_kv"
+    ws2 = torch.empty(cp.ring_prefill_workspace_size(gq, P, other, True), dtype=torch.uint8, device=dev)
+    cp.ring_prefill(gq, gk, gv, P, other, True, out=out, lse=lse, workspace=ws2)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    reps = max(1, args.steps // 2)
+    for _ in range(reps):
+        cp.ring_prefill(gq, gk, gv, P, other, True, out=out, lse=lse, workspace=ws2)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    result[other] = {"ms_per_step": round(dt * 1e3, 3), "TFLOP/s": round(total_flops / dt / 1e12, 2)}
+    del ws2, ws
+
+    if not args.no_decode:
+        wd = si.WORKLOADS[DECODE]
+        log(f"[bench] drawing {wd.name} inputs")
+        dq_, dk_, dv_ = si.make_qkv(wd)
+        dq, dk, dv = dq_.to(dev), dk_.to(dev), dv_.to(dev)
+        del dq_, dk_, dv_
+        dws = torch.empty(cp.splitkv_decode_workspace_size(dq, dk, wd.n_chunks), dtype=torch.uint8, device=dev)
+        dout = torch.empty(wd.q_shape(), dtype=torch.float32, device=dev)
+        dlse = torch.empty(wd.q_shape()[:3], dtype=torch.float32, device=dev)
+        for _ in range(3):
+            cp.splitkv_decode(dq, dk, dv, wd.n_chunks, out=dout, lse=dlse, workspace=dws)
+        torch.cuda.synchronize()
+        reps = max(5, args.steps)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        for i in range(reps):
+            ev[i][0].record(stream)
+            cp.splitkv_decode(dq, dk, dv, wd.n_chunks, out=dout, lse=dlse, workspace=dws)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        ms = sorted(e[0].elapsed_time(e[1]) for e in ev)[reps // 2]
+        kv_bytes = 2 * wd.B * wd.Skv * wd.Hkv * wd.D * 2
+        q_bytes = wd.B * wd.Hq * wd.D * 2
+        part_bytes = wd.n_chunks * wd.B * wd.Hq * (wd.D + 1) * 4
+        out_bytes = wd.B * wd.Hq * (wd.D + 1) * 4
+        dec_bytes = kv_bytes + q_bytes + 2 * part_bytes + out_bytes
+        gbs = dec_bytes / (ms * 1e-3) / 1e9
+        result["decode"] = {"workload": wd.name, "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                            "ms": round(ms, 4), "algorithmic_bytes": dec_bytes, "peak_GB/s": PEAK_HBM_GBS}
+        log(f"[bench] decode {ms:.3f} ms, {gbs:.0f} GB/s")
+        del dq, dk, dv, dws
+
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = COPY_BYTES
+
+    if not args.no_cpu_baseline:
+        log(f"[bench] timing the fp64 oracle on the host (~{args.cpu_seconds:.0f} s)")
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def _pmc_rows(d: str):
+    rows = []
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    if not rows:
+        raise SystemExit(f"no *counter_collection.csv under {d}")
+    return rows
+
+
+def _per_dispatch(rows, counter: str, name_part: str):
+    vals = [float(r["Counter_Value"]) for r in rows
+            if r.get("Counter_Name") == counter and name_part in r.get("Kernel_Name", "")]
+    return sum(vals) / len(vals) if vals else None, len(vals)
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str) -> int:
+    """HBM bytes per partial-kernel launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    each scaled by what the same counter reads for the 1 GiB copy kernel."""
+    fr, wr = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
+    f_k, nf = _per_dispatch(fr, "FETCH_SIZE", "partial_bf16_kernel")
+    w_k, nw = _per_dispatch(wr, "WRITE_SIZE", "partial_bf16_kernel")
+    f_c, _ = _per_dispatch(fr, "FETCH_SIZE", "elementwise")
+    w_c, _ = _per_dispatch(wr, "WRITE_SIZE", "elementwise")
+    if None in (f_k, w_k, f_c, w_c):
+        raise SystemExit("missing counters for the partial kernel or the copy kernel")
+    f_scale = COPY_BYTES / (f_c * 1024.0)
+    w_scale = COPY_BYTES / (w_c * 1024.0)
+    fetch_b = f_k * 1024.0 * f_scale
+    write_b = w_k * 1024.0 * w_scale
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("# HBM traffic of partial_bf16_kernel<128> per launch on the 128K-token workload, Pass-KV\n")
+        f.write("# from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs of:\n")
+        f.write("#   python bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-decode --calibrate-copy\n")
+        f.write("# each counter scaled by its reading for a plain 1 GiB fp32 copy kernel\n")
+        f.write(f"kernel_source_sha256_16: {kernel_hash()}\n")
+        f.write(f"dispatches: {nf} (FETCH) {nw} (WRITE)\n")
+        f.write(f"fetch_kib_per_dispatch_raw: {f_k:.1f}\n")
+        f.write(f"write_kib_per_dispatch_raw: {w_k:.1f}\n")
+        f.write(f"copy_fetch_scale: {f_scale:.4f}\n")
+        f.write(f"copy_write_scale: {w_scale:.4f}\n")
+        f.write(f"fetch_bytes_per_launch: {fetch_b:.0f}\n")
+        f.write(f"write_bytes_per_launch: {write_b:.0f}\n")
+        f.write(f"hbm_bytes_per_launch: {fetch_b + write_b:.0f}\n")
+    print(open(TRAFFIC_FILE).read())
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

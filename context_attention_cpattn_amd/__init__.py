@@ -18,6 +18,7 @@ import torch
 
 __all__ = [
     "CpattnError", "LIB_PATH", "version", "partial", "merge", "ring_prefill", "ring_prefill_workspace_size",
+    "ring_step", "ring_merge",
     "splitkv_decode", "splitkv_decode_workspace_size", "PASS_KV", "PASS_Q", "MAX_MERGE",
 ]
 
@@ -50,7 +51,7 @@ class Tensor(ctypes.Structure):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
-                          "(python -m context_attention_cpattn_amd._build)")
+                          "(python context_attention_cpattn_amd/_build.py)")
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER(Tensor)
     i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
@@ -59,6 +60,8 @@ def _load() -> ctypes.CDLL:
         "cpattn_merge": ([P, P, i32, P, P, vp], i32),
         "cpattn_ring_prefill_workspace_size": ([P, i32, i32, i32], sz),
         "cpattn_ring_prefill": ([P, P, P, i32, i32, i32, P, P, vp, sz, vp], i32),
+        "cpattn_ring_step": ([P, P, P, i32, i32, i32, i32, vp, sz, vp], i32),
+        "cpattn_ring_merge": ([i32, i32, i32, vp, sz, P, P, vp], i32),
         "cpattn_splitkv_decode_workspace_size": ([P, P, i32], sz),
         "cpattn_splitkv_decode": ([P, P, P, i32, P, P, vp, sz, vp], i32),
         "cpattn_last_error": ([], ctypes.c_char_p),
@@ -171,6 +174,23 @@ def ring_prefill(q, k, v, n_chunks: int, order="pass_kv", causal: bool = True, o
     _check(lib.cpattn_ring_prefill(_ref(dq), _ref(dk), _ref(dv), int(n_chunks), _ORDERS[order], int(bool(causal)),
                                    _ref(do), _ref(dl), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                    _stream(q, stream)))
+    return out, lse
+
+
+def ring_step(q, k, v, n_chunks: int, step: int, workspace, order="pass_kv", causal: bool = True, stream=None):
+    """Partial attention of every rank's pair at ring step ``step`` into ``workspace``."""
+    dq, dk, dv = describe(q), describe(k), describe(v)
+    _check(lib.cpattn_ring_step(_ref(dq), _ref(dk), _ref(dv), int(n_chunks), _ORDERS[order], int(bool(causal)),
+                                int(step), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                _stream(q, stream)))
+
+
+def ring_merge(n_chunks: int, workspace, out, lse=None, order="pass_kv", causal: bool = True, stream=None):
+    """Merge each Q chunk's partials (filled by ``ring_step`` over all steps) into ``out``/``lse``."""
+    do, dl = describe(out), describe(lse, True)
+    _check(lib.cpattn_ring_merge(int(n_chunks), _ORDERS[order], int(bool(causal)), workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(), _ref(do), _ref(dl),
+                                 _stream(out, stream)))
     return out, lse
 
 

@@ -1,6 +1,7 @@
 """Build libcpattn.so (HIP kernels + C ABI) for gfx950 with hipcc.
 
-Usage: ``python -m context_attention_cpattn_amd._build`` or ``build()``.
+Usage: ``python context_attention_cpattn_amd/_build.py`` (run as a script, so the
+package -- which loads the library -- is not imported first) or ``build()``.
 Objects go to ``_build/`` at the repository root; the shared library is
 written next to this file, where the Python binding loads it from.
 """

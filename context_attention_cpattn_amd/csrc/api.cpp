@@ -339,50 +339,63 @@ size_t cpattn_ring_prefill_workspace_size(const cpattn_tensor* q, int n_chunks, 
   return ring_layout(*q, n_chunks, causal != 0).bytes;
 }
 
-cpattn_status cpattn_ring_prefill(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
-                                  int n_chunks, cpattn_order order, int causal, cpattn_tensor* out,
-                                  cpattn_tensor* lse, void* workspace, size_t workspace_bytes, void* stream) {
+cpattn_status cpattn_ring_step(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                               int n_chunks, cpattn_order order, int causal, int step, void* workspace,
+                               size_t workspace_bytes, void* stream) {
   cpattn_status s;
   if ((s = check_ring(q, k, v, n_chunks, order, causal)) != CPATTN_OK) return s;
-  if ((s = check_out(out, lse, *q, true, false)) != CPATTN_OK) return s;
+  if (step < 0 || step >= n_chunks) return fail(CPATTN_ERR_INVALID_ARG, "step %d outside [0, %d)", step, n_chunks);
+  if (q->S == 0 || q->B == 0) return ok();
   const bool cz = causal != 0;
   const RingLayout L = ring_layout(*q, n_chunks, cz);
-  if (q->S == 0 || q->B == 0) return ok();
   if ((s = check_workspace(workspace, workspace_bytes, L.bytes)) != CPATTN_OK) return s;
 
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const int P = n_chunks;
-  float* ws_o = static_cast<float*>(workspace);
-  float* ws_l = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.o_bytes);
-
-  // partials, one launch per ring step (all ranks of the step together)
   cpattn::PartialLaunch a = base_partial(*q, *k, *v);
-  a.o = ws_o;
-  a.lse = ws_l;
+  a.o = static_cast<float*>(workspace);
+  a.lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.o_bytes);
   a.o_sh = q->D; a.o_ss = q->H * q->D; a.o_sb = L.C * q->H * q->D;
   a.l_sh = 1; a.l_ss = q->H; a.l_sb = L.C * q->H;
   a.o_slot = L.slot_o;
   a.l_slot = L.slot_l;
-  a.q_pos0 = 0;
-  a.kv_pos0 = 0;
   a.chunk_len = L.C;
   a.Sq = (int32_t)L.C;
   a.Sk = (int32_t)L.C;
   a.causal = causal;
-  std::vector<std::vector<int>> arrivals(P);
-  for (int step = 0; step < P; ++step) {
-    const std::vector<Pair> items = ring_step(P, step, order, cz);
-    a.n_items = 0;
-    for (const Pair& p : items) {
-      a.items[a.n_items++] = cpattn::Item{p.q, p.kv, (int32_t)ring_slot(P, p.q, p.kv, cz)};
-      arrivals[p.q].push_back(p.kv);
-    }
-    if (a.n_items == 0) continue;
-    const hipError_t e = launch_partial(a, q->dtype, (int)q->D, (int)L.C, st);
-    if (e != hipSuccess) return hip_fail(e, "ring step launch");
-  }
+  a.n_items = 0;
+  for (const Pair& p : ring_step(n_chunks, step, order, cz))
+    a.items[a.n_items++] = cpattn::Item{p.q, p.kv, (int32_t)ring_slot(n_chunks, p.q, p.kv, cz)};
+  if (a.n_items == 0) return ok();
+  const hipError_t e = launch_partial(a, q->dtype, (int)q->D, (int)L.C, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ring step launch");
+  return ok();
+}
 
-  // each owner merges its partials in arrival order
+cpattn_status cpattn_ring_merge(int n_chunks, cpattn_order order, int causal, const void* workspace,
+                                size_t workspace_bytes, cpattn_tensor* out, cpattn_tensor* lse, void* stream) {
+  cpattn_status s;
+  if (n_chunks < 1) return fail(CPATTN_ERR_INVALID_ARG, "n_chunks must be >= 1");
+  if (n_chunks > cpattn::kMaxMerge)
+    return fail(CPATTN_ERR_UNSUPPORTED, "n_chunks above %d not supported", cpattn::kMaxMerge);
+  if (order != CPATTN_PASS_KV && order != CPATTN_PASS_Q) return fail(CPATTN_ERR_INVALID_ARG, "unknown ring order");
+  if (causal != 0 && causal != 1) return fail(CPATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if ((s = check_tensor(out, "out", false)) != CPATTN_OK) return s;
+  if (out->D != 64 && out->D != 128)
+    return fail(CPATTN_ERR_UNSUPPORTED, "head_dim %lld not supported (64 or 128)", (long long)out->D);
+  if ((s = check_out(out, lse, *out, true, false)) != CPATTN_OK) return s;
+  if (out->S % n_chunks != 0)
+    return fail(CPATTN_ERR_INVALID_ARG, "sequence length %lld not divisible by n_chunks %d", (long long)out->S, n_chunks);
+  if (out->S == 0 || out->B == 0) return ok();
+  const bool cz = causal != 0;
+  const RingLayout L = ring_layout(*out, n_chunks, cz);
+  if ((s = check_workspace(const_cast<void*>(workspace), workspace_bytes, L.bytes)) != CPATTN_OK) return s;
+
+  const int P = n_chunks;
+  const float* ws_o = static_cast<const float*>(workspace);
+  const float* ws_l = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + L.o_bytes);
+  std::vector<std::vector<int>> arrivals(P);
+  for (int step = 0; step < P; ++step)
+    for (const Pair& p : ring_step(P, step, order, cz)) arrivals[p.q].push_back(p.kv);
+
   for (int i = 0; i < P; ++i) {
     cpattn::MergeLaunch m;
     std::memset(&m, 0, sizeof m);
@@ -393,19 +406,34 @@ cpattn_status cpattn_ring_prefill(const cpattn_tensor* q, const cpattn_tensor* k
       m.lse[c] = ws_l + slot * L.slot_l;
     }
     m.out_bf16 = out->dtype == CPATTN_BF16;
-    m.B = (int32_t)q->B; m.S = (int32_t)L.C; m.H = (int32_t)q->H; m.D = (int32_t)q->D;
-    m.p_sb = a.o_sb; m.p_ss = a.o_ss; m.p_sh = a.o_sh;
-    m.pl_sb = a.l_sb; m.pl_ss = a.l_ss; m.pl_sh = a.l_sh;
+    m.B = (int32_t)out->B; m.S = (int32_t)L.C; m.H = (int32_t)out->H; m.D = (int32_t)out->D;
+    m.p_sh = out->D; m.p_ss = out->H * out->D; m.p_sb = L.C * out->H * out->D;
+    m.pl_sh = 1; m.pl_ss = out->H; m.pl_sb = L.C * out->H;
     m.out = static_cast<char*>(out->data) + (size_t)(i * L.C * out->stride_s) * elem_bytes(out->dtype);
     m.o_sb = out->stride_b; m.o_ss = out->stride_s; m.o_sh = out->stride_h;
     if (lse != nullptr) {
       m.out_lse = static_cast<float*>(lse->data) + i * L.C * lse->stride_s;
       m.ol_sb = lse->stride_b; m.ol_ss = lse->stride_s; m.ol_sh = lse->stride_h;
     }
-    const hipError_t e = cpattn::launch_merge(m, st);
+    const hipError_t e = cpattn::launch_merge(m, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "ring merge launch");
   }
   return ok();
+}
+
+cpattn_status cpattn_ring_prefill(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                                  int n_chunks, cpattn_order order, int causal, cpattn_tensor* out,
+                                  cpattn_tensor* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  cpattn_status s;
+  if ((s = check_ring(q, k, v, n_chunks, order, causal)) != CPATTN_OK) return s;
+  if ((s = check_out(out, lse, *q, true, false)) != CPATTN_OK) return s;
+  if (q->S == 0 || q->B == 0) return ok();
+  if ((s = check_workspace(workspace, workspace_bytes, ring_layout(*q, n_chunks, causal != 0).bytes)) != CPATTN_OK)
+    return s;
+  for (int step = 0; step < n_chunks; ++step)
+    if ((s = cpattn_ring_step(q, k, v, n_chunks, order, causal, step, workspace, workspace_bytes, stream)) != CPATTN_OK)
+      return s;
+  return cpattn_ring_merge(n_chunks, order, causal, workspace, workspace_bytes, out, lse, stream);
 }
 
 size_t cpattn_splitkv_decode_workspace_size(const cpattn_tensor* q, const cpattn_tensor* k, int n_chunks) {

@@ -150,6 +150,31 @@ cpattn_status cpattn_ring_prefill(const cpattn_tensor* q, const cpattn_tensor* k
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * cpattn_ring_step - the partial-attention work of one ring step for every
+ * simulated rank: the pairs that step s assigns (as in cpattn_ring_prefill)
+ * are computed in one launch into their workspace slots.  Running steps
+ * 0 .. n_chunks-1 and then cpattn_ring_merge on the same workspace is exactly
+ * cpattn_ring_prefill; on a real CP ring this is what a rank does between two
+ * K/V (or Q) exchanges ("Context Parallelism for Million-Token Contexts").
+ * Arguments as in cpattn_ring_prefill; 0 <= step < n_chunks.  A step with no
+ * causally visible pair enqueues nothing.
+ */
+cpattn_status cpattn_ring_step(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                               int n_chunks, cpattn_order order, int causal, int step,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * cpattn_ring_merge - merge every Q chunk's partials from a workspace filled
+ * by cpattn_ring_step (all steps), in the order they reached the chunk's
+ * owner, into out [B, S, Hq, D] (F32 or BF16) and lse [B, S, Hq] (F32, or
+ * NULL).  The shapes come from out; n_chunks, order and causal must match the
+ * steps that filled the workspace.
+ */
+cpattn_status cpattn_ring_merge(int n_chunks, cpattn_order order, int causal,
+                                const void* workspace, size_t workspace_bytes,
+                                cpattn_tensor* out, cpattn_tensor* lse, void* stream);
+
+/*
  * cpattn_splitkv_decode_workspace_size - bytes of workspace
  * cpattn_splitkv_decode needs (0 if the arguments are invalid).
  */
