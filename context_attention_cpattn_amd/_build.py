@@ -26,6 +26,9 @@ COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     # packed fp32 VALU ops stay off in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in arch VGPRs: the softmax reads S directly, and the
+    # 32-row, two-waves-per-SIMD kernels fit in 256 registers without AGPRs
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 

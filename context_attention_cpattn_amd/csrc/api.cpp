@@ -115,7 +115,7 @@ cpattn::PartialLaunch base_partial(const cpattn_tensor& q, const cpattn_tensor& 
 
 hipError_t launch_partial(const cpattn::PartialLaunch& a, int dtype, int D, int Sq, hipStream_t st) {
   if (dtype == CPATTN_BF16) {
-    const int rpb = cpattn::partial_bf16_rows_per_block();
+    const int rpb = cpattn::partial_bf16_rows_per_block(D);
     return cpattn::launch_partial_bf16(a, D, (Sq + rpb - 1) / rpb, st);
   }
   const int rpb = cpattn::partial_f32_rows_per_block(D);

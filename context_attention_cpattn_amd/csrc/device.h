@@ -67,6 +67,18 @@ __device__ __forceinline__ void st_lds8(uint8_t* p, const u32x2& v) { *reinterpr
 // Value of the lane 32 positions away (lanes 0..31 <-> 32..63).
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 
+// max / sum of a value and its copy in the lane 32 positions away, through
+// v_permlane32_swap: swapping the upper half of x with the lower half of a
+// second copy of x leaves {x[l mod 32], x[l mod 32 + 32]} in the two results.
+__device__ __forceinline__ float pair32_max(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup w runs on
 // XCD w % 8).  Give each XCD a contiguous range of logical tiles so tiles that
 // share K/V (adjacent heads of one query tile) share that XCD's L2.

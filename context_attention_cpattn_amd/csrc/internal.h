@@ -74,7 +74,7 @@ hipError_t launch_partial_f32(const PartialLaunch& a, int D, int n_qtiles, hipSt
 hipError_t launch_merge(const MergeLaunch& a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeLaunch& a, int D, hipStream_t s);
 
-int partial_bf16_rows_per_block();  // query rows per workgroup of the bf16 kernel
+int partial_bf16_rows_per_block(int D);  // query rows per workgroup of the bf16 kernel
 int partial_f32_rows_per_block(int D);
 
 }  // namespace cpattn
