@@ -52,8 +52,8 @@ cpattn_status check_tensor(const cpattn_tensor* t, const char* name, bool lse) {
   if (t->stride_b < 0 || t->stride_s < 0 || t->stride_h < 0)
     return fail(CPATTN_ERR_INVALID_ARG, "%s: negative stride", name);
   if (lse && t->D != 1) return fail(CPATTN_ERR_INVALID_ARG, "%s: an LSE tensor must have D == 1", name);
-  if (t->B > INT32_MAX || t->S > INT32_MAX || t->H > INT32_MAX)
-    return fail(CPATTN_ERR_UNSUPPORTED, "%s: sizes beyond 2^31-1 are not supported", name);
+  if (t->B > INT32_MAX || t->S >= (int64_t(1) << 30) || t->H > INT32_MAX)
+    return fail(CPATTN_ERR_UNSUPPORTED, "%s: sequence lengths of 2^30 or more (or B, H beyond 2^31-1) are not supported", name);
   if (numel(*t) == 0) return ok();
   if (t->data == nullptr) return fail(CPATTN_ERR_INVALID_ARG, "%s: data is NULL", name);
   const uintptr_t p = reinterpret_cast<uintptr_t>(t->data);

@@ -64,6 +64,20 @@ __device__ __forceinline__ u32x2 ld_lds8(const uint8_t* p) { return *reinterpret
 __device__ __forceinline__ void st_lds16(uint8_t* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ void st_lds8(uint8_t* p, const u32x2& v) { *reinterpret_cast<u32x2*>(p) = v; }
 
+// 16 bytes from global memory straight into LDS (global_load_lds_dwordx4):
+// lane i of the wave writes LDS bytes [lds_base + 16 i, lds_base + 16 i + 16).
+// Issued through inline assembly so the compiler does not drain every
+// outstanding load before it (it cannot tell which LDS bytes a pending
+// transfer writes); the caller waits with s_waitcnt vmcnt before using the
+// data.  lds_base must be wave-uniform.
+__device__ __forceinline__ void gload_lds16(const void* gptr, uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
+}
+
 // Value of the lane 32 positions away (lanes 0..31 <-> 32..63).
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 
