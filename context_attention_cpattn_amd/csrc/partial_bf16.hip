@@ -321,7 +321,17 @@ __global__ __launch_bounds__(256) void partial_bf16_kernel(const PartialLaunch a
 #define CPATTN_D128_STAGES 3  // LDS stages of the plain D = 128 kernel
 #endif
 #ifndef CPATTN_D128_PIPE
-#define CPATTN_D128_PIPE 3   // 0: plain, 1: software-pipelined, 2: ping-pong, 3: direct-to-LDS K and V, 3 stages
+#define CPATTN_D128_PIPE 4   // 0: plain, 1: software-pipelined, 2: ping-pong, 3: direct-to-LDS K and V, 3 stages,
+                             // 4: as 3 with MFMA / VALU interleaved inside each wave
+#endif
+#ifndef CPATTN_V4_KLA
+#define CPATTN_V4_KLA 4
+#endif
+#ifndef CPATTN_V4_VLA
+#define CPATTN_V4_VLA 4
+#endif
+#ifndef CPATTN_D128_V4_STAGES
+#define CPATTN_D128_V4_STAGES 3
 #endif
 #ifndef CPATTN_PIPE_VALU
 #define CPATTN_PIPE_VALU 7   // softmax VALU instructions issued after each MFMA of the next tile
@@ -1319,6 +1329,327 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_v3_kernel(const Partial
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// D = 128 kernel, fourth form: the third form's data movement (K and V
+// direct to LDS, V^T through the transposing read), with each wave's work
+// software-pipelined so that its matrix and vector work overlap.  Iteration t
+// runs two phases:
+//   A: S(t+1) = K(t+1) Q^T on the matrix cores, while the vector unit packs
+//      P(t) to bf16 and adds it to the row sums;
+//   B: O^T += V(t)^T P(t)^T on the matrix cores, while the vector unit takes
+//      the row maxima of S(t+1), moves the running reference and evaluates
+//      the exponentials P(t+1).
+// Each MFMA is followed by its slice of the vector work, and a scheduling
+// fence after every slice keeps the compiler from regrouping them.  The O
+// rescale a moved reference needs (rare, see kTau) runs after phase B, once
+// P(t) has been accumulated against the old reference.
+// ---------------------------------------------------------------------------
+// Empty asm that claims to rewrite x: the value must be computed before this
+// point (passes that sink or hoist code cannot move it past), which keeps the
+// vector work of the pipelined loop in the slot it was written in.
+template <class T>
+__device__ __forceinline__ void pin(T& x) {
+  asm volatile("" : "+v"(x));
+}
+
+template <int NST>
+__global__ __launch_bounds__(512) void partial_bf16_d128_v4_kernel(const PartialLaunch a, const int n_qtiles) {
+  constexpr int D = 128, BN = 64, NDS = 8, NT = 512, BM = 256;
+  constexpr int TBYTES = BN * D * 2;  // one K or V tile
+  constexpr int STAGE = 2 * TBYTES;   // K then V
+  constexpr int KLA = CPATTN_V4_KLA;            // K operand reads issued this many MFMAs ahead
+  constexpr int VLA = CPATTN_V4_VLA;            // V operand reads issued this many MFMAs ahead
+  constexpr float SCALE_LOG2 = 0.12751743082459868f;
+  static_assert(NST == 3 || NST == 4, "3 or 4 LDS stages");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NST * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+
+  const int bh = a.B * a.Hq;
+  const int per_item = bh * n_qtiles;
+  const int L = xcd_logical_block(blockIdx.x, per_item * a.n_items);
+  const int item = L / per_item;
+  int rem = L - item * per_item;
+  const int qt = n_qtiles - 1 - rem / bh;
+  rem = rem % bh;
+  const int b = rem / a.Hq;
+  const int h = rem - b * a.Hq;
+  const int kvh = h / a.G;
+  const Item it = a.items[item];
+
+  const __bf16* qp = static_cast<const __bf16*>(a.q) + b * a.q_sb + h * a.q_sh +
+                     (int64_t)it.q_chunk * a.chunk_len * a.q_ss;
+  const __bf16* kp = static_cast<const __bf16*>(a.k) + b * a.k_sb + kvh * a.k_sh +
+                     (int64_t)it.kv_chunk * a.chunk_len * a.k_ss;
+  const __bf16* vp = static_cast<const __bf16*>(a.v) + b * a.v_sb + kvh * a.v_sh +
+                     (int64_t)it.kv_chunk * a.chunk_len * a.v_ss;
+  float* op = a.o + it.slot * a.o_slot + b * a.o_sb + h * a.o_sh;
+  float* lp = a.lse + it.slot * a.l_slot + b * a.l_sb + h * a.l_sh;
+  const int64_t qpos0 = a.q_pos0 + (int64_t)it.q_chunk * a.chunk_len;
+  const int64_t kvpos0 = a.kv_pos0 + (int64_t)it.kv_chunk * a.chunk_len;
+
+  const int dpos = (int)max<int64_t>(-(1 << 30), min<int64_t>(1 << 30, kvpos0 - qpos0));
+  const int m0 = qt * BM;
+  const int r0 = m0 + wave * 32;
+  const int row = r0 + l32;
+
+  int n_end = a.Sk;
+  if (a.causal) n_end = max(0, min(a.Sk, min(m0 + BM, a.Sq) - dpos));
+  const int n_tiles = (n_end + BN - 1) / BN;
+
+  f32x16 o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o[db] = (f32x16){};
+  float m = kNegInf;  // running reference (log2 domain) of this lane's row
+  float l = 0.f;      // this lane's share of the row sum, relative to m
+
+  if (n_tiles > 0) {
+    bf16x8 qf[NDS];
+    {
+      const __bf16* qr = qp + (int64_t)row * a.q_ss + 8 * g;
+      const bool ok = row < a.Sq;
+#pragma unroll
+      for (int s2 = 0; s2 < NDS; ++s2) qf[s2] = ok ? as_bf16x8(ld_global16(qr + 16 * s2)) : (bf16x8){};
+    }
+    int koff[NDS];
+#pragma unroll
+    for (int s2 = 0; s2 < NDS; ++s2) koff[s2] = l32 * 256 + (((2 * s2 + g) ^ (l32 & 15)) << 4);
+    int voff[4];
+    {
+      const int s16 = lane & 15, ks = s16 >> 2, c16 = l32 >> 4, c8 = (s16 & 3) >> 1, bo = (s16 & 1) * 8;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        voff[db] = TBYTES + (4 * g + ks) * 256 + ((4 * (db ^ ks) + 2 * c16 + c8) << 4) + bo;
+    }
+    // Fetch: 16-byte slot i*NT + wave*64 + lane of a tile holds key slot>>4 at
+    // physical chunk slot&15.  The source pointers advance one tile per fetch.
+    int fkey[2];
+    const __bf16* kf[2];
+    const __bf16* vf[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int slot = i * NT + wave * 64 + lane;
+      fkey[i] = slot >> 4;
+      kf[i] = kp + fkey[i] * a.k_ss + (((slot & 15) ^ (fkey[i] & 15)) << 3);
+      vf[i] = vp + fkey[i] * a.v_ss + (((slot & 15) ^ (4 * (fkey[i] & 3))) << 3);
+    }
+    const int64_t kstep = (int64_t)BN * a.k_ss, vstep = (int64_t)BN * a.v_ss;
+    const uint32_t lbase = lds_addr(smem) + wave * 64 * 16;
+    int n_fetched = 0;
+    auto fetch = [&](int stage) {
+      const uint32_t dst = lbase + stage * STAGE;
+      if ((n_fetched + 1) * BN <= a.Sk) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          gload_lds16(kf[i], dst + i * NT * 16);
+          gload_lds16(vf[i], dst + i * NT * 16 + TBYTES);
+        }
+      } else {
+        // rows past the block end re-read the last row: their scores are masked
+        // to -inf, so their p is exactly 0
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int over = max(0, n_fetched * BN + fkey[i] - (a.Sk - 1));
+          gload_lds16(kf[i] - over * a.k_ss, dst + i * NT * 16);
+          gload_lds16(vf[i] - over * a.v_ss, dst + i * NT * 16 + TBYTES);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        kf[i] += kstep;
+        vf[i] += vstep;
+      }
+      ++n_fetched;
+    };
+
+    auto mask_tile = [&](f32x16 (&sc)[2], int t) -> bool {
+      const int n0 = t * BN;
+      if (n0 + BN > a.Sk || (a.causal && dpos + n0 + BN - 1 > r0)) {
+        int lim = a.Sk - n0;
+        if (a.causal) lim = min(lim, row - dpos - n0 + 1);
+        mask_block<2>(sc, max(0, min(lim, BN)), g);
+        return true;
+      }
+      return false;
+    };
+
+    // Scores of the newest tile (sn), the packed probabilities of the tile
+    // being accumulated (pw: word w holds p[2w], p[2w+1] of this lane's 32
+    // keys, words 0..7 from key block 0, 8..15 from key block 1), and the
+    // state of the reference move made for the newest tile.
+    f32x16 sn[2];
+    uint32_t pw[16];
+    bool need = false;
+    float alpha = 1.f;
+    float mref = 0.f;
+    // max over scores f0 .. f1-1 of key block kb (mx must already hold a value
+    // unless this starts at score 0 of key block 0)
+    auto part_max = [&](float& mx, int kb, int f0, int f1) {
+#pragma unroll
+      for (int f = f0; f < f1; ++f) mx = (kb == 0 && f == 0) ? sn[0][0] : fmaxf(mx, sn[kb][f]);
+    };
+    // reference move for the newest tile: the row sum is rescaled at once, O
+    // before the next PV phase (the current one still adds old-reference terms)
+    auto move_ref = [&](float mx) {
+      mx = pair32_max(mx);
+      const float mt = mx * SCALE_LOG2;
+      need = __any(mt > m + kTau);
+      const float m_new = need ? fmaxf(m, mt) : m;
+      alpha = (m_new == m) ? 1.f : fast_exp2(m - m_new);
+      l *= alpha;
+      m = m_new;
+      mref = (m == kNegInf) ? 0.f : m;
+    };
+    // probabilities of scores 2w, 2w+1 of key block kb -> packed word, row sum
+    auto prob_pair = [&](const f32x16& x, int w) -> uint32_t {
+      const float p0 = fast_exp2(fmaf(x[2 * w], SCALE_LOG2, -mref));
+      const float p1 = fast_exp2(fmaf(x[2 * w + 1], SCALE_LOG2, -mref));
+      l += p0 + p1;
+      return pack_bf16(p0, p1);
+    };
+
+    // prologue: tiles 0 .. NST-2 in flight, wait for tiles 0 and 1
+#pragma unroll
+    for (int i = 0; i < NST - 1; ++i)
+      if (i < n_tiles) fetch(i);
+    if (NST == 4 && n_tiles > 2)
+      asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    {
+      sn[0] = (f32x16){};
+      sn[1] = (f32x16){};
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        sn[j >> 3] = mfma32(as_bf16x8(ld_lds16(smem + koff[j & 7] + (j >> 3) * 8192)), qf[j & 7], sn[j >> 3]);
+      mask_tile(sn, 0);
+      float mx;
+      part_max(mx, 0, 0, 16);
+      part_max(mx, 1, 0, 16);
+      move_ref(mx);
+#pragma unroll
+      for (int w = 0; w < 8; ++w) pw[w] = prob_pair(sn[0], w);
+    }
+
+    // Iteration t.  The last one also computes scores for the tile after the
+    // last: every one of them is masked (that tile starts at or past the
+    // block's last visible key), so its max is -inf, the reference stays and
+    // its probabilities are 0; its K operands come from a stale stage.
+    auto iteration = [&](int t, auto st_tag) {
+      constexpr int ST = decltype(st_tag)::value;
+      constexpr int SN = (ST + 1) % NST;
+      constexpr int SL = (ST + NST - 1) % NST;
+      const uint8_t* cur = smem + ST * STAGE;
+      const uint8_t* nxt = smem + SN * STAGE;
+      const bool do_fetch = t + NST - 1 < n_tiles;
+      if (do_fetch) fetch(SL);
+
+      u32x4 kop[16];
+      u32x2 vlo[16], vhi[16];
+      auto read_v = [&](int jj) {  // operands of PV MFMA jj: u = jj >> 2, db = jj & 3
+        const int u = jj >> 2, db = jj & 3;
+        vlo[jj] = ld_lds8_tr(cur + voff[db] + (16 * u) * 256);
+        vhi[jj] = ld_lds8_tr(cur + voff[db] + (16 * u + 8) * 256);
+      };
+      // ---- phase A: S(t+1) = K(t+1) Q^T; key block 1 of P(t) ----
+      const f32x16 s1 = sn[1];  // scores of tile t, key block 1
+      f32x16 x[2] = {(f32x16){}, (f32x16){}};
+#pragma unroll
+      for (int j = 0; j < KLA; ++j) kop[j] = ld_lds16(nxt + koff[j & 7] + (j >> 3) * 8192);
+      __builtin_amdgcn_sched_barrier(0);
+      float mx0 = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (j + KLA < 16) kop[j + KLA] = ld_lds16(nxt + koff[(j + KLA) & 7] + ((j + KLA) >> 3) * 8192);
+        if (j >= 16 - VLA) read_v(j - (16 - VLA));
+        x[j >> 3] = mfma32(as_bf16x8(kop[j]), qf[j & 7], x[j >> 3]);
+        if (j < 8) {
+          pw[8 + j] = prob_pair(s1, j);
+          pin(pw[8 + j]);
+          pin(l);
+        }
+        if (j >= 9) {
+          // running max over key block 0 of tile t+1 (done by the 8th MFMA)
+#pragma unroll
+          for (int f = (j == 9) ? 0 : 2 * j - 16; f < 2 * j - 14; ++f) mx0 = (f == 0) ? x[0][0] : fmaxf(mx0, x[0][f]);
+          pin(mx0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      sn[0] = x[0];
+      sn[1] = x[1];
+      if (mask_tile(sn, t + 1)) part_max(mx0, 0, 0, 16);
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- phase B: O^T += V(t)^T P(t)^T; row max, reference, key block 0 of P(t+1) ----
+      uint32_t pn[8];
+      float mx = mx0;
+      // O still holds terms against the reference before the last move
+      if (need) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[db] *= alpha;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        if (jj + VLA < 16) read_v(jj + VLA);
+        const int u = jj >> 2, db = jj & 3;
+        const u32x4 av = {vlo[jj][0], vlo[jj][1], vhi[jj][0], vhi[jj][1]};
+        const u32x4 bp = {pw[4 * u], pw[4 * u + 1], pw[4 * u + 2], pw[4 * u + 3]};
+        o[db] = mfma32(as_bf16x8(av), as_bf16x8(bp), o[db]);
+        if (jj <= 1) {
+          part_max(mx, 1, 8 * jj, 8 * jj + 8);
+          pin(mx);
+        } else if (jj == 2) {
+          move_ref(mx);
+          pin(l);
+          pin(alpha);
+          pin(mref);
+        } else if (jj <= 10) {
+          pn[jj - 3] = prob_pair(sn[0], jj - 3);
+          pin(pn[jj - 3]);
+          pin(l);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int w = 0; w < 8; ++w) pw[w] = pn[w];
+      // tile t+2 must have landed; fetches of later tiles stay in flight
+      if (NST == 4 && do_fetch)
+        asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+    for (int t = 0; t < n_tiles; t += NST) {
+      iteration(t, std::integral_constant<int, 0>{});
+      if (t + 1 < n_tiles) iteration(t + 1, std::integral_constant<int, 1>{});
+      if (t + 2 < n_tiles) iteration(t + 2, std::integral_constant<int, 2>{});
+      if constexpr (NST == 4)
+        if (t + 3 < n_tiles) iteration(t + 3, std::integral_constant<int, 3 % NST>{});
+    }
+  }
+
+  const float l_tot = pair32_sum(l);
+  if (row < a.Sq) {
+    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    float* orow = op + (int64_t)row * a.o_ss;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4 v4 = {o[db][4 * i4 + 0] * inv, o[db][4 * i4 + 1] * inv, o[db][4 * i4 + 2] * inv,
+                          o[db][4 * i4 + 3] * inv};
+        *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * i4 + 4 * g) = v4;
+      }
+    if (g == 0) lp[(int64_t)row * a.l_ss] = (l_tot > 0.f) ? (m + fast_log2(l_tot)) * kLn2 : kNegInf;
+  }
+}
+
 }  // namespace
 
 int partial_bf16_rows_per_block(int D) { return D == 128 ? CPATTN_D128_NW * 32 : 128; }
@@ -1328,7 +1659,10 @@ hipError_t launch_partial_bf16(const PartialLaunch& a, int D, int n_qtiles, hipS
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (D == 128)
-    if (CPATTN_D128_PIPE == 3)
+    if (CPATTN_D128_PIPE == 4)
+      hipLaunchKernelGGL(partial_bf16_d128_v4_kernel<CPATTN_D128_V4_STAGES>, dim3((unsigned)blocks), dim3(512), 0, s, a,
+                         n_qtiles);
+    else if (CPATTN_D128_PIPE == 3)
       hipLaunchKernelGGL(partial_bf16_d128_v3_kernel, dim3((unsigned)blocks), dim3(512), 0, s, a, n_qtiles);
     else if (CPATTN_D128_PIPE == 2)
       hipLaunchKernelGGL(partial_bf16_d128_pp_kernel, dim3((unsigned)blocks), dim3(512), 0, s, a, n_qtiles);
