@@ -196,7 +196,7 @@ def main(argv=None) -> int:
     traffic = read_traffic()
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "kernel": "partial_bf16_d128_v3_kernel", "launches_per_step": P,
+                "kernel": "partial_bf16_d128_kernel", "launches_per_step": P,
                 "avg_launch_ms": round(avg_launch_ms, 4),
                 "algorithmic_flop_per_launch": total_flops / P}
     per_step_tflops = [round(step_flops[s] / (sum(k_ms[i][s] for i in range(args.steps)) / args.steps * 1e-3) / 1e12, 1)
@@ -305,8 +305,8 @@ def summarize_pmc(fetch_dir: str, write_dir: str) -> int:
     """HBM bytes per partial-kernel launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
     each scaled by what the same counter reads for the 1 GiB copy kernel."""
     fr, wr = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
-    f_k, nf = _per_dispatch(fr, "FETCH_SIZE", "partial_bf16_d128_v3_kernel")
-    w_k, nw = _per_dispatch(wr, "WRITE_SIZE", "partial_bf16_d128_v3_kernel")
+    f_k, nf = _per_dispatch(fr, "FETCH_SIZE", "partial_bf16_d128_kernel")
+    w_k, nw = _per_dispatch(wr, "WRITE_SIZE", "partial_bf16_d128_kernel")
     f_c, _ = _per_dispatch(fr, "FETCH_SIZE", "elementwise")
     w_c, _ = _per_dispatch(wr, "WRITE_SIZE", "elementwise")
     if None in (f_k, w_k, f_c, w_c):
