@@ -317,7 +317,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str) -> int:
     write_b = w_k * 1024.0 * w_scale
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
-        f.write("# HBM traffic of partial_bf16_kernel<128> per launch on the 128K-token workload, Pass-KV\n")
+        f.write("# HBM traffic of partial_bf16_d128_kernel per launch on the 128K-token workload, Pass-KV\n")
         f.write("# from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs of:\n")
         f.write("#   python bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-decode --calibrate-copy\n")
         f.write("# each counter scaled by its reading for a plain 1 GiB fp32 copy kernel\n")

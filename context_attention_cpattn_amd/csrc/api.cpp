@@ -194,8 +194,11 @@ DecodeLayout decode_layout(const cpattn_tensor& q, const cpattn_tensor& k, int n
   const int64_t chunk = k.S / n_chunks;
   const int64_t base_units = q.B * k.H * L.head_blocks * n_chunks;
   int ns = 1;
-  // enough waves to keep every CU streaming, but keep splits >= 256 keys
-  while (base_units * ns < 4096 && chunk / (2 * ns) >= 256 && (int64_t)n_chunks * ns * 2 <= cpattn::kMaxMerge) ns *= 2;
+  // The decode kernel runs one persistent workgroup per CU that streams its
+  // units back to back; about four units per CU of a 256-CU device balance
+  // the load without cutting the stream into many short units.  Splits stay
+  // >= 256 keys.
+  while (base_units * ns < 1024 && chunk / (2 * ns) >= 256 && (int64_t)n_chunks * ns * 2 <= cpattn::kMaxMerge) ns *= 2;
   L.n_split = ns;
   const int64_t per = (chunk + ns - 1) / ns;
   L.split_len = (int)((per + 31) / 32 * 32);

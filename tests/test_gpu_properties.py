@@ -125,14 +125,15 @@ def test_decode_lse_of_zero_query(cp):
     assert (o.double() - mean).abs().max().item() < 1e-5
 
 
-@pytest.mark.parametrize("B,Skv,G,Hkv,n", [(3, 1000, 16, 1, 4), (2, 4096, 8, 2, 8), (1, 2048, 40, 1, 2),
-                                            (5, 96, 16, 1, 3), (2, 8192, 16, 1, 1)])
-def test_decode_shapes(cp, B, Skv, G, Hkv, n):
-    q = si.draw_tensor(11, 0, (B, 1, G * Hkv, 128), torch.bfloat16)
-    k = si.draw_tensor(11, 1, (B, Skv, Hkv, 128), torch.bfloat16)
-    v = si.draw_tensor(11, 2, (B, Skv, Hkv, 128), torch.bfloat16)
+@pytest.mark.parametrize("B,Skv,G,Hkv,n,D", [(3, 1000, 16, 1, 4, 128), (2, 4096, 8, 2, 8, 128), (1, 2048, 40, 1, 2, 128),
+                                              (5, 96, 16, 1, 3, 128), (2, 8192, 16, 1, 1, 128), (300, 512, 16, 1, 2, 128),
+                                              (3, 1000, 16, 1, 4, 64), (2, 4096, 8, 2, 8, 64), (1, 2048, 40, 1, 2, 64)])
+def test_decode_shapes(cp, B, Skv, G, Hkv, n, D):
+    q = si.draw_tensor(11, 0, (B, 1, G * Hkv, D), torch.bfloat16)
+    k = si.draw_tensor(11, 1, (B, Skv, Hkv, D), torch.bfloat16)
+    v = si.draw_tensor(11, 2, (B, Skv, Hkv, D), torch.bfloat16)
     o_ref, l_ref = oracle.splitkv_decode(q, k, v, n)
-    banner("decode", B, Skv, G, Hkv, n)
+    banner("decode", B, Skv, G, Hkv, n, D)
     o, l = cp.splitkv_decode(q.to(DEV), k.to(DEV), v.to(DEV), n)
     torch.cuda.synchronize()
-    compare(o, l, o_ref, l_ref, BF16_TOL, f"decode B{B} Skv{Skv} G{G} Hkv{Hkv} n{n}")
+    compare(o, l, o_ref, l_ref, BF16_TOL, f"decode B{B} Skv{Skv} G{G} Hkv{Hkv} n{n} D{D}")
