@@ -6,6 +6,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -266,6 +267,36 @@ cpattn_status cpattn_partial(const cpattn_tensor* q, const cpattn_tensor* k, con
   if (causal != 0 && causal != 1) return fail(CPATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
   if (q->S == 0 || q->B == 0) return ok();
 
+  // One query row per sequence (a decode-shaped call) with at most 64 query
+  // heads per KV head goes to the split-KV decode kernel as a single partial:
+  // its query heads share each K/V read, where the prefill kernel would give
+  // every head a 256-row workgroup of its own.  The row sees the key prefix
+  // [0, visible).
+  const int64_t G = q->H / k->H;
+  if (q->S == 1 && q->dtype == CPATTN_BF16 && (q->D == 64 || q->D == 128) && G <= 64) {
+    int64_t visible = k->S;
+    if (causal) visible = std::max<int64_t>(0, std::min<int64_t>(k->S, q_offset - kv_offset + 1));
+    cpattn::DecodeLaunch d;
+    std::memset(&d, 0, sizeof d);
+    d.q = q->data; d.k = k->data; d.v = v->data;
+    d.o = static_cast<float*>(out->data);
+    d.lse = static_cast<float*>(lse->data);
+    d.o_slot = 0; d.o_sb = out->stride_b; d.o_sh = out->stride_h;
+    d.l_slot = 0; d.l_sb = lse->stride_b; d.l_sh = lse->stride_h;
+    d.q_sb = q->stride_b; d.q_sh = q->stride_h;
+    d.k_sb = k->stride_b; d.k_ss = k->stride_s; d.k_sh = k->stride_h;
+    d.v_sb = v->stride_b; d.v_ss = v->stride_s; d.v_sh = v->stride_h;
+    d.B = (int32_t)q->B; d.Hq = (int32_t)q->H; d.Hkv = (int32_t)k->H; d.G = (int32_t)G;
+    d.Skv = (int32_t)visible;
+    d.n_chunks = 1;
+    d.n_split = 1;
+    d.split_len = (int32_t)((std::max<int64_t>(visible, 1) + 63) / 64 * 64);
+    d.head_blocks = (int32_t)((G + 15) / 16);
+    const hipError_t e = cpattn::launch_decode_bf16(d, (int)q->D, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "partial attention (one query row) launch");
+    return ok();
+  }
+
   cpattn::PartialLaunch a = base_partial(*q, *k, *v);
   a.o = static_cast<float*>(out->data);
   a.lse = static_cast<float*>(lse->data);
@@ -471,6 +502,8 @@ cpattn_status cpattn_splitkv_decode(const cpattn_tensor* q, const cpattn_tensor*
   std::memset(&d, 0, sizeof d);
   d.q = q->data; d.k = k->data; d.v = v->data;
   d.o = ws_o; d.lse = ws_l;
+  d.o_slot = q->B * q->H * q->D; d.o_sb = q->H * q->D; d.o_sh = q->D;
+  d.l_slot = q->B * q->H; d.l_sb = q->H; d.l_sh = 1;
   d.q_sb = q->stride_b; d.q_sh = q->stride_h;
   d.k_sb = k->stride_b; d.k_ss = k->stride_s; d.k_sh = k->stride_h;
   d.v_sb = v->stride_b; d.v_ss = v->stride_s; d.v_sh = v->stride_h;

@@ -270,12 +270,12 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeLaunch a
     l_tot += __shfl_xor(l_tot, 32);
     if (head_ok) {
       const int p_idx = U.c * a.n_split + U.sp;
-      const int64_t rowi = (int64_t)p_idx * a.B * a.Hq + (int64_t)U.b * a.Hq + h;
-      float* orow = a.o + rowi * D + wave * (D / 4);
+      float* orow = a.o + p_idx * a.o_slot + U.b * a.o_sb + h * a.o_sh + wave * (D / 4);
       const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) *reinterpret_cast<f32x4*>(orow + db * 16 + 4 * g4) = oacc[db] * inv;
-      if (wave == 0 && g4 == 0) a.lse[rowi] = (l_tot > 0.f) ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
+      if (wave == 0 && g4 == 0)
+        a.lse[p_idx * a.l_slot + U.b * a.l_sb + h * a.l_sh] = (l_tot > 0.f) ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
     }
   }
 }

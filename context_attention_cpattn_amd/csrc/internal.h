@@ -57,8 +57,10 @@ struct DecodeLaunch {
   const void* q;  // bf16 [B, 1, Hq, D]
   const void* k;  // bf16 [B, Skv, Hkv, D]
   const void* v;
-  float* o;       // workspace partials: [n_part][B][Hq][D]
-  float* lse;     // workspace LSE:      [n_part][B][Hq]
+  float* o;       // partial p, batch b, head h at o + p*o_slot + b*o_sb + h*o_sh (D contiguous)
+  float* lse;     // partial LSE at lse + p*l_slot + b*l_sb + h*l_sh
+  int64_t o_slot, o_sb, o_sh;
+  int64_t l_slot, l_sb, l_sh;
   int64_t q_sb, q_sh;
   int64_t k_sb, k_ss, k_sh;
   int64_t v_sb, v_ss, v_sh;

@@ -90,6 +90,9 @@ typedef struct cpattn_tensor {
  *   lse [B, Sq, Hq]      F32 (D = 1): natural-log LSE of this block's scores
  * q_offset, kv_offset >= 0; causal is 0 or 1.  Rows that see no key of this
  * block (possible under the causal mask) get out = 0 and lse = -inf.
+ * A BF16 call with Sq = 1, D in {64, 128} and Hq / Hkv <= 64 (a decode-shaped
+ * block) runs on the split-KV decode kernel, whose query heads share each
+ * K/V read; the result is the same up to rounding.
  */
 cpattn_status cpattn_partial(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
                              int64_t q_offset, int64_t kv_offset, int causal,

@@ -39,6 +39,10 @@ PARTIAL_CASES = [
     (1, 256, 256, 2, 1, 64, 0, 0, True),         # D = 64
     (2, 190, 300, 4, 4, 64, 150, 0, True),       # D = 64, GQA off, ragged
     (1, 1, 1000, 16, 1, 128, 999, 0, True),      # one query row (decode-like shape)
+    (3, 1, 777, 16, 1, 128, 500, 0, True),       # one row seeing a ragged key prefix (501 keys)
+    (2, 1, 300, 8, 2, 128, 10, 50, True),        # one row before the block: all masked
+    (2, 1, 300, 40, 1, 128, 0, 0, False),        # one row, 40 heads per KV head (3 head blocks)
+    (4, 1, 513, 16, 1, 64, 600, 0, True),        # one row, D = 64
     (1, 64, 0, 2, 1, 128, 0, 0, True),           # empty K/V block
 ]
 
@@ -59,18 +63,20 @@ def test_partial_matches_oracle(cp, case, dtype):
     compare(o, l, o_ref, l_ref, BF16_TOL if dtype == "bf16" else F32_TOL, f"partial {dtype} {case}")
 
 
-def test_partial_strided_views(cp):
-    """Non-contiguous views (head-sliced, padded rows) through the descriptor strides."""
+@pytest.mark.parametrize("Sq", [200, 1])
+def test_partial_strided_views(cp, Sq):
+    """Non-contiguous views (head-sliced, padded rows) through the descriptor strides;
+    Sq = 1 takes the one-row (decode kernel) route."""
     B, S, H, D = 2, 200, 6, 128
-    big_q = draw(77, (B, S, H + 2, D), torch.bfloat16, 0)
+    big_q = draw(77, (B, Sq, H + 2, D), torch.bfloat16, 0)
     big_k = draw(77, (B, S, 3, D), torch.bfloat16, 1)
     big_v = draw(77, (B, S, 3, D), torch.bfloat16, 2)
     q, k, v = big_q[:, :, 1:H + 1], big_k[:, :, 1:3], big_v[:, :, 1:3]
     o_ref, l_ref = oracle.partial_attention(q, k, v, 10, 0, True)
     gq, gk, gv = big_q.to(DEV)[:, :, 1:H + 1], big_k.to(DEV)[:, :, 1:3], big_v.to(DEV)[:, :, 1:3]
-    out_big = torch.full((B, S, H + 1, D), float("nan"), device=DEV)
-    lse_big = torch.full((B, S, H + 3), float("nan"), device=DEV)
-    banner("partial strided")
+    out_big = torch.full((B, Sq, H + 1, D), float("nan"), device=DEV)
+    lse_big = torch.full((B, Sq, H + 3), float("nan"), device=DEV)
+    banner("partial strided", Sq)
     o, l = cp.partial(gq, gk, gv, 10, 0, True, out=out_big[:, :, :H], lse=lse_big[:, :, 2:2 + H])
     torch.cuda.synchronize()
     compare(o, l, o_ref, l_ref, BF16_TOL, "partial strided")
