@@ -13,7 +13,9 @@ The same JSON line also carries the dominant kernel's roofline (partial
 attention, measured with HIP events around each ring-step launch on the
 stream the library launches on), the split-KV decode leg (GB/s on the
 128 x 32768-key decode workload), the Pass-Q ordering of the prefill, the
-merge kernel's bandwidth, and the fp64 CPU oracle timed on a bounded sample.
+8K-token GQA workload (and, with --with-1m, the 1M-token one) as whole ring
+prefills, the merge kernel's bandwidth, and the fp64 CPU oracle timed on a
+bounded sample.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1]
   python bench.py --summarize-pmc FETCH_DIR WRITE_DIR   # traffic summary from two rocprofv3 --pmc runs
@@ -126,6 +128,9 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-small", action="store_true", help="skip the 8K-token GQA workload leg")
+    ap.add_argument("--with-1m", action="store_true",
+                    help="also time the 1M-token workload (about a minute more: inputs are 4 GiB of Q)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB fp32 copy kernel (counter calibration under rocprofv3 --pmc)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -238,6 +243,39 @@ def main(argv=None) -> int:
     dt = (time.perf_counter() - t0) / reps
     result[other] = {"ms_per_step": round(dt * 1e3, 3), "TFLOP/s": round(total_flops / dt / 1e12, 2)}
     del ws2, ws
+
+    def prefill_leg(name: str, reps: int):
+        """Median time of whole Pass-KV ring prefills of another workload (2 warm-ups)."""
+        wx = si.WORKLOADS[name]
+        log(f"[bench] drawing {wx.name} inputs")
+        xq_, xk_, xv_ = si.make_qkv(wx)
+        xq, xk, xv = xq_.to(dev), xk_.to(dev), xv_.to(dev)
+        del xq_, xk_, xv_
+        xws = torch.empty(cp.ring_prefill_workspace_size(xq, wx.n_chunks, "pass_kv", True), dtype=torch.uint8,
+                          device=dev)
+        xout = torch.empty(wx.q_shape(), dtype=torch.float32, device=dev)
+        xlse = torch.empty(wx.q_shape()[:3], dtype=torch.float32, device=dev)
+        for _ in range(2):
+            cp.ring_prefill(xq, xk, xv, wx.n_chunks, "pass_kv", True, out=xout, lse=xlse, workspace=xws)
+        torch.cuda.synchronize()
+        evx = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        for i in range(reps):
+            evx[i][0].record(stream)
+            cp.ring_prefill(xq, xk, xv, wx.n_chunks, "pass_kv", True, out=xout, lse=xlse, workspace=xws)
+            evx[i][1].record(stream)
+            torch.cuda.synchronize()
+            log(f"[bench] {wx.name} rep {i + 1}/{reps}: {evx[i][0].elapsed_time(evx[i][1]):.3f} ms")
+        msx = sorted(e[0].elapsed_time(e[1]) for e in evx)[reps // 2]
+        tf = wx.flops() / (msx * 1e-3) / 1e12
+        del xq, xk, xv, xws, xout, xlse
+        torch.cuda.empty_cache()
+        return {"workload": wx.name, "order": "pass_kv", "ms": round(msx, 4), "TFLOP/s": round(tf, 2),
+                "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2), "flop": wx.flops(), "reps": reps}
+
+    if not args.no_small:
+        result["gqa_8k"] = prefill_leg("gqa16_bf16_s8k_p8", max(5, args.steps))
+    if args.with_1m:
+        result["prefill_1m"] = prefill_leg("prefill_bf16_s1m_p8", 3)
 
     if not args.no_decode:
         wd = si.WORKLOADS[DECODE]

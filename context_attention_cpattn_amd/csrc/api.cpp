@@ -373,6 +373,33 @@ size_t cpattn_ring_prefill_workspace_size(const cpattn_tensor* q, int n_chunks, 
   return ring_layout(*q, n_chunks, causal != 0).bytes;
 }
 
+// Partial attention of the given (q-chunk, kv-chunk) pairs into their
+// workspace slots, in launches of at most kMaxItems pairs.
+cpattn_status launch_ring_items(const cpattn_tensor& q, const cpattn_tensor& k, const cpattn_tensor& v,
+                                const RingLayout& L, int n_chunks, bool causal, const std::vector<Pair>& pairs,
+                                void* workspace, void* stream, const char* what) {
+  cpattn::PartialLaunch a = base_partial(q, k, v);
+  a.o = static_cast<float*>(workspace);
+  a.lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.o_bytes);
+  a.o_sh = q.D; a.o_ss = q.H * q.D; a.o_sb = L.C * q.H * q.D;
+  a.l_sh = 1; a.l_ss = q.H; a.l_sb = L.C * q.H;
+  a.o_slot = L.slot_o;
+  a.l_slot = L.slot_l;
+  a.chunk_len = L.C;
+  a.Sq = (int32_t)L.C;
+  a.Sk = (int32_t)L.C;
+  a.causal = causal ? 1 : 0;
+  size_t i = 0;
+  while (i < pairs.size()) {
+    a.n_items = 0;
+    for (; i < pairs.size() && a.n_items < cpattn::kMaxItems; ++i)
+      a.items[a.n_items++] = cpattn::Item{pairs[i].q, pairs[i].kv, (int32_t)ring_slot(n_chunks, pairs[i].q, pairs[i].kv, causal)};
+    const hipError_t e = launch_partial(a, q.dtype, (int)q.D, (int)L.C, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, what);
+  }
+  return ok();
+}
+
 cpattn_status cpattn_ring_step(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
                                int n_chunks, cpattn_order order, int causal, int step, void* workspace,
                                size_t workspace_bytes, void* stream) {
@@ -384,24 +411,8 @@ cpattn_status cpattn_ring_step(const cpattn_tensor* q, const cpattn_tensor* k, c
   const RingLayout L = ring_layout(*q, n_chunks, cz);
   if ((s = check_workspace(workspace, workspace_bytes, L.bytes)) != CPATTN_OK) return s;
 
-  cpattn::PartialLaunch a = base_partial(*q, *k, *v);
-  a.o = static_cast<float*>(workspace);
-  a.lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.o_bytes);
-  a.o_sh = q->D; a.o_ss = q->H * q->D; a.o_sb = L.C * q->H * q->D;
-  a.l_sh = 1; a.l_ss = q->H; a.l_sb = L.C * q->H;
-  a.o_slot = L.slot_o;
-  a.l_slot = L.slot_l;
-  a.chunk_len = L.C;
-  a.Sq = (int32_t)L.C;
-  a.Sk = (int32_t)L.C;
-  a.causal = causal;
-  a.n_items = 0;
-  for (const Pair& p : ring_step(n_chunks, step, order, cz))
-    a.items[a.n_items++] = cpattn::Item{p.q, p.kv, (int32_t)ring_slot(n_chunks, p.q, p.kv, cz)};
-  if (a.n_items == 0) return ok();
-  const hipError_t e = launch_partial(a, q->dtype, (int)q->D, (int)L.C, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "ring step launch");
-  return ok();
+  return launch_ring_items(*q, *k, *v, L, n_chunks, cz, ring_step(n_chunks, step, order, cz), workspace, stream,
+                           "ring step launch");
 }
 
 cpattn_status cpattn_ring_merge(int n_chunks, cpattn_order order, int causal, const void* workspace,
@@ -464,9 +475,28 @@ cpattn_status cpattn_ring_prefill(const cpattn_tensor* q, const cpattn_tensor* k
   if (q->S == 0 || q->B == 0) return ok();
   if ((s = check_workspace(workspace, workspace_bytes, ring_layout(*q, n_chunks, causal != 0).bytes)) != CPATTN_OK)
     return s;
+  // On one device the pairs of all ring steps are independent, so they go
+  // out together; each lands in its own slot, and the merge reads the slots
+  // in the ring order's arrival order.  The workgroups of a launch are dealt
+  // to the XCDs in contiguous eighths of the grid, so the diagonal pairs
+  // (half the work of a full pair under the causal mask) are spread evenly
+  // through the list: every eighth gets its share of them.
+  const bool cz = causal != 0;
+  std::vector<Pair> full, diag;
   for (int step = 0; step < n_chunks; ++step)
-    if ((s = cpattn_ring_step(q, k, v, n_chunks, order, causal, step, workspace, workspace_bytes, stream)) != CPATTN_OK)
-      return s;
+    for (const Pair& p : ring_step(n_chunks, step, order, cz)) (cz && p.q == p.kv ? diag : full).push_back(p);
+  std::vector<Pair> pairs;
+  pairs.reserve(full.size() + diag.size());
+  const size_t n = full.size() + diag.size();
+  size_t fi = 0, di = 0;
+  for (size_t i = 0; i < n; ++i) {
+    // diagonal pair number d goes to position floor((d + 0.5) * n / n_diag)
+    const bool take_diag = di < diag.size() && (fi == full.size() || (2 * di + 1) * n <= 2 * i * diag.size() + diag.size());
+    pairs.push_back(take_diag ? diag[di++] : full[fi++]);
+  }
+  if ((s = launch_ring_items(*q, *k, *v, ring_layout(*q, n_chunks, cz), n_chunks, cz, pairs, workspace, stream,
+                             "ring prefill launch")) != CPATTN_OK)
+    return s;
   return cpattn_ring_merge(n_chunks, order, causal, workspace, workspace_bytes, out, lse, stream);
 }
 

@@ -7,7 +7,7 @@
 
 namespace cpattn {
 
-constexpr int kMaxItems = 64;   // partial-attention work items per launch
+constexpr int kMaxItems = 160;  // partial-attention work items per launch (kernel argument ~2 KB)
 constexpr int kMaxMerge = 64;   // partials per merge launch (CPATTN_MAX_MERGE)
 
 // One (Q block, K/V block) pair of a launch.  Pointers are derived from the
