@@ -434,35 +434,25 @@ cpattn_status cpattn_ring_merge(int n_chunks, cpattn_order order, int causal, co
   const RingLayout L = ring_layout(*out, n_chunks, cz);
   if ((s = check_workspace(const_cast<void*>(workspace), workspace_bytes, L.bytes)) != CPATTN_OK) return s;
 
-  const int P = n_chunks;
-  const float* ws_o = static_cast<const float*>(workspace);
-  const float* ws_l = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + L.o_bytes);
-  std::vector<std::vector<int>> arrivals(P);
-  for (int step = 0; step < P; ++step)
-    for (const Pair& p : ring_step(P, step, order, cz)) arrivals[p.q].push_back(p.kv);
-
-  for (int i = 0; i < P; ++i) {
-    cpattn::MergeLaunch m;
-    std::memset(&m, 0, sizeof m);
-    m.n = (int32_t)arrivals[i].size();
-    for (int c = 0; c < m.n; ++c) {
-      const int64_t slot = ring_slot(P, i, arrivals[i][c], cz);
-      m.o[c] = ws_o + slot * L.slot_o;
-      m.lse[c] = ws_l + slot * L.slot_l;
-    }
-    m.out_bf16 = out->dtype == CPATTN_BF16;
-    m.B = (int32_t)out->B; m.S = (int32_t)L.C; m.H = (int32_t)out->H; m.D = (int32_t)out->D;
-    m.p_sh = out->D; m.p_ss = out->H * out->D; m.p_sb = L.C * out->H * out->D;
-    m.pl_sh = 1; m.pl_ss = out->H; m.pl_sb = L.C * out->H;
-    m.out = static_cast<char*>(out->data) + (size_t)(i * L.C * out->stride_s) * elem_bytes(out->dtype);
-    m.o_sb = out->stride_b; m.o_ss = out->stride_s; m.o_sh = out->stride_h;
-    if (lse != nullptr) {
-      m.out_lse = static_cast<float*>(lse->data) + i * L.C * lse->stride_s;
-      m.ol_sb = lse->stride_b; m.ol_ss = lse->stride_s; m.ol_sh = lse->stride_h;
-    }
-    const hipError_t e = cpattn::launch_merge(m, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "ring merge launch");
+  cpattn::RingMergeLaunch m;
+  std::memset(&m, 0, sizeof m);
+  m.ws_o = static_cast<const float*>(workspace);
+  m.ws_l = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + L.o_bytes);
+  m.slot_o = L.slot_o;
+  m.slot_l = L.slot_l;
+  m.P = n_chunks;
+  m.C = (int32_t)L.C; m.B = (int32_t)out->B; m.H = (int32_t)out->H; m.D = (int32_t)out->D;
+  m.causal = cz ? 1 : 0;
+  m.pass_q = order == CPATTN_PASS_Q ? 1 : 0;
+  m.out_bf16 = out->dtype == CPATTN_BF16;
+  m.out = out->data;
+  m.o_sb = out->stride_b; m.o_ss = out->stride_s; m.o_sh = out->stride_h;
+  if (lse != nullptr) {
+    m.out_lse = static_cast<float*>(lse->data);
+    m.ol_sb = lse->stride_b; m.ol_ss = lse->stride_s; m.ol_sh = lse->stride_h;
   }
+  const hipError_t e = cpattn::launch_ring_merge(m, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ring merge launch");
   return ok();
 }
 

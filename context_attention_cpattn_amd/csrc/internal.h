@@ -53,6 +53,22 @@ struct MergeLaunch {
   int64_t ol_sb, ol_ss, ol_sh;
 };
 
+// Merge of a ring's workspace slots into the final output: every owner i
+// merges its partials in the ring order's arrival order (computed in the
+// kernel), all owners in one launch.
+struct RingMergeLaunch {
+  const float* ws_o;          // slot t: O [B][C][H][D] at ws_o + t * slot_o
+  const float* ws_l;          // slot t: LSE [B][C][H] at ws_l + t * slot_l
+  int64_t slot_o, slot_l;
+  int32_t P, C, B, H, D;
+  int32_t causal, pass_q;     // ring order: 0 = Pass-KV, 1 = Pass-Q
+  int32_t out_bf16;
+  void* out;                  // [B][P*C][H][D]
+  int64_t o_sb, o_ss, o_sh;
+  float* out_lse;             // may be null
+  int64_t ol_sb, ol_ss, ol_sh;
+};
+
 struct DecodeLaunch {
   const void* q;  // bf16 [B, 1, Hq, D]
   const void* k;  // bf16 [B, Skv, Hkv, D]
@@ -74,6 +90,7 @@ struct DecodeLaunch {
 hipError_t launch_partial_bf16(const PartialLaunch& a, int D, int n_qtiles, hipStream_t s);
 hipError_t launch_partial_f32(const PartialLaunch& a, int D, int n_qtiles, hipStream_t s);
 hipError_t launch_merge(const MergeLaunch& a, hipStream_t s);
+hipError_t launch_ring_merge(const RingMergeLaunch& a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeLaunch& a, int D, hipStream_t s);
 
 int partial_bf16_rows_per_block(int D);  // query rows per workgroup of the bf16 kernel

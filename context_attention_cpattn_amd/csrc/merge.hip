@@ -7,12 +7,59 @@
 // out = sum_c w_c O_c / sum_c w_c and lse = M + ln(sum_c w_c).
 //
 // Bandwidth bound: D/4 threads per row, each streaming 16 bytes of every
-// partial; sums run in partial order (deterministic).
+// partial, eight partials' loads in flight at a time; sums run in partial
+// order (deterministic).
 #include "device.h"
 #include "internal.h"
 
 namespace cpattn {
 namespace {
+
+// One row's merge, shared by both kernels so they round identically.  The
+// partials' LSEs give M first; then the O pieces are read in batches of 8
+// (all loads of a batch issued before any is used, for memory-level
+// parallelism) and accumulated in partial order.  o_at(c) / l_at(c) give the
+// c-th partial's 16 bytes of this thread and its LSE.
+template <class OAt, class LAt>
+__device__ __forceinline__ void merge_row(int n, OAt o_at, LAt l_at, f32x4& res, float& M, float& den) {
+  M = kNegInf;
+  for (int c = 0; c < n; ++c) M = fmaxf(M, l_at(c));
+  f32x4 acc = (f32x4){};
+  den = 0.f;
+  if (M != kNegInf) {
+    for (int c0 = 0; c0 < n; c0 += 8) {
+      f32x4 v[8];
+      float lw[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (c0 + u < n) {
+          v[u] = o_at(c0 + u);
+          lw[u] = l_at(c0 + u);
+        }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (c0 + u < n) {
+          const float w = fast_exp2((lw[u] - M) * kLog2e);
+          den += w;
+          acc[0] = fmaf(w, v[u][0], acc[0]);
+          acc[1] = fmaf(w, v[u][1], acc[1]);
+          acc[2] = fmaf(w, v[u][2], acc[2]);
+          acc[3] = fmaf(w, v[u][3], acc[3]);
+        }
+    }
+  }
+  const float inv = (den > 0.f) ? 1.f / den : 0.f;
+  res = acc * inv;
+}
+
+__device__ __forceinline__ void store_row(void* out, bool out_bf16, int64_t off, const f32x4& r) {
+  if (out_bf16) {
+    const u32x2 pk = {pack_bf16(r[0], r[1]), pack_bf16(r[2], r[3])};
+    *reinterpret_cast<u32x2*>(static_cast<__bf16*>(out) + off) = pk;
+  } else {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + off) = r;
+  }
+}
 
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeLaunch a) {
@@ -30,33 +77,55 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeLaunch a) {
 
   const int64_t loff = b * a.pl_sb + s * a.pl_ss + h * a.pl_sh;
   const int64_t ooff = b * a.p_sb + s * a.p_ss + h * a.p_sh + 4 * part;
-  float M = kNegInf;
-  for (int c = 0; c < a.n; ++c) M = fmaxf(M, a.lse[c][loff]);
-
-  f32x4 acc = (f32x4){};
-  float den = 0.f;
-  if (M != kNegInf) {
-    for (int c = 0; c < a.n; ++c) {
-      const float w = fast_exp2((a.lse[c][loff] - M) * kLog2e);
-      const f32x4 v = *reinterpret_cast<const f32x4*>(a.o[c] + ooff);
-      den += w;
-      acc[0] = fmaf(w, v[0], acc[0]);
-      acc[1] = fmaf(w, v[1], acc[1]);
-      acc[2] = fmaf(w, v[2], acc[2]);
-      acc[3] = fmaf(w, v[3], acc[3]);
-    }
-  }
-  const float inv = (den > 0.f) ? 1.f / den : 0.f;
-  const f32x4 r = acc * inv;
-  const int64_t out_off = b * a.o_sb + s * a.o_ss + h * a.o_sh + 4 * part;
-  if (a.out_bf16) {
-    const u32x2 pk = {pack_bf16(r[0], r[1]), pack_bf16(r[2], r[3])};
-    *reinterpret_cast<u32x2*>(static_cast<__bf16*>(a.out) + out_off) = pk;
-  } else {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + out_off) = r;
-  }
+  f32x4 r;
+  float M, den;
+  merge_row(
+      a.n, [&](int c) { return *reinterpret_cast<const f32x4*>(a.o[c] + ooff); }, [&](int c) { return a.lse[c][loff]; },
+      r, M, den);
+  store_row(a.out, a.out_bf16, b * a.o_sb + s * a.o_ss + h * a.o_sh + 4 * part, r);
   if (a.out_lse != nullptr && part == 0)
     a.out_lse[b * a.ol_sb + s * a.ol_ss + h * a.ol_sh] = (den > 0.f) ? M + fast_log2(den) * kLn2 : kNegInf;
+}
+
+// The c-th partial to reach owner i: Pass-KV sends K/V down the ring, so at
+// step s owner i holds kv chunk (i - s) mod P; Pass-Q sends Q, so at step s
+// the rank holding kv chunk (i + s) mod P computes owner i's piece.  Under
+// the causal mask only kv <= i exists: Pass-KV sees i, i-1, ..., 0 and
+// Pass-Q sees i, then 0, 1, ..., i-1.
+__device__ __forceinline__ int arrival_kv(const RingMergeLaunch& a, int i, int c) {
+  if (a.causal) return a.pass_q ? (c == 0 ? i : c - 1) : i - c;
+  return a.pass_q ? (i + c) % a.P : (i - c + a.P) % a.P;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void ring_merge_kernel(const RingMergeLaunch a) {
+  constexpr int TPR = D / 4;
+  constexpr int RPB = 256 / TPR;
+  const int tid = threadIdx.x;
+  const int part = tid % TPR;
+  const int64_t row = (int64_t)blockIdx.x * RPB + tid / TPR;
+  const int64_t per_owner = (int64_t)a.B * a.C * a.H;
+  if (row >= per_owner * a.P) return;
+  const int i = (int)(row / per_owner);
+  const int64_t r = row - i * per_owner;  // row of owner i's slots, [B][C][H] order
+  const int h = (int)(r % a.H);
+  const int64_t bs = r / a.H;
+  const int s = (int)(bs % a.C);
+  const int b = (int)(bs / a.C);
+  const int n = a.causal ? i + 1 : a.P;
+  auto slot = [&](int c) -> int64_t {
+    const int kv = arrival_kv(a, i, c);
+    return a.causal ? (int64_t)i * (i + 1) / 2 + kv : (int64_t)i * a.P + kv;
+  };
+  f32x4 res;
+  float M, den;
+  merge_row(
+      n, [&](int c) { return *reinterpret_cast<const f32x4*>(a.ws_o + slot(c) * a.slot_o + r * D + 4 * part); },
+      [&](int c) { return a.ws_l[slot(c) * a.slot_l + r]; }, res, M, den);
+  const int64_t sg = (int64_t)i * a.C + s;  // row of the full sequence
+  store_row(a.out, a.out_bf16, b * a.o_sb + sg * a.o_ss + h * a.o_sh + 4 * part, res);
+  if (a.out_lse != nullptr && part == 0)
+    a.out_lse[b * a.ol_sb + sg * a.ol_ss + h * a.ol_sh] = (den > 0.f) ? M + fast_log2(den) * kLn2 : kNegInf;
 }
 
 }  // namespace
@@ -71,6 +140,20 @@ hipError_t launch_merge(const MergeLaunch& a, hipStream_t s) {
     hipLaunchKernelGGL(merge_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, s, a);
   else if (a.D == 64)
     hipLaunchKernelGGL(merge_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_merge(const RingMergeLaunch& a, hipStream_t s) {
+  const long long rows = (long long)a.P * a.B * a.C * a.H;
+  if (rows <= 0) return hipSuccess;
+  const long long blocks = (rows * (a.D / 4) + 255) / 256;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (a.D == 128)
+    hipLaunchKernelGGL(ring_merge_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  else if (a.D == 64)
+    hipLaunchKernelGGL(ring_merge_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

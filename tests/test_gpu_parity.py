@@ -153,6 +153,28 @@ def test_ring_small_orders(cp, P, order, causal):
     assert torch.equal(o16.cpu(), o.cpu().to(torch.bfloat16))
 
 
+@pytest.mark.parametrize("P,order,causal", [(4, "pass_kv", True), (4, "pass_q", True), (3, "pass_kv", False),
+                                            (3, "pass_q", False), (9, "pass_kv", True)])
+def test_ring_merge_follows_arrival_order(cp, P, order, causal):
+    """The ring driver's merge equals, bit for bit, merging the same partials in the
+    arrival order the oracle's schedule defines (partials via the partial entry point)."""
+    C, H, D = 96, 2, 128
+    S = C * P
+    q = draw(61 + P, (1, S, H, D), torch.bfloat16, 0).to(DEV)
+    k = draw(61 + P, (1, S, 1, D), torch.bfloat16, 1).to(DEV)
+    v = draw(61 + P, (1, S, 1, D), torch.bfloat16, 2).to(DEV)
+    banner("ring merge order", P, order, causal)
+    o, l = cp.ring_prefill(q, k, v, P, order, causal)
+    arrivals = oracle.arrival_order(P, order, causal)
+    for i in range(P):
+        parts = [cp.partial(q[:, i * C:(i + 1) * C], k[:, j * C:(j + 1) * C], v[:, j * C:(j + 1) * C], i * C, j * C, causal)
+                 for j in arrivals[i]]
+        om, lm = cp.merge([p_[0] for p_ in parts], [p_[1] for p_ in parts])
+        torch.cuda.synchronize()
+        assert torch.equal(om, o[:, i * C:(i + 1) * C]), f"owner {i}: O differs"
+        assert torch.equal(lm, l[:, i * C:(i + 1) * C]), f"owner {i}: LSE differs"
+
+
 def test_workload_gqa_8k(cp):
     w = si.WORKLOADS["gqa16_bf16_s8k_p8"]
     q, k, v = si.make_qkv(w)
