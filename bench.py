@@ -74,21 +74,25 @@ def ring_step_flops(w, order: str):
     return out
 
 
-def read_traffic():
-    """Per-launch HBM traffic of the partial kernel from the committed pmc summary, if current."""
+def read_pmc_summary():
+    """(HBM bytes per launch, shader clock GHz) of the partial kernel from the committed pmc
+    summary, each None if absent or if the kernel source changed since it was taken."""
     if not os.path.exists(TRAFFIC_FILE):
-        return None
+        return None, None
     kv = {}
     for ln in open(TRAFFIC_FILE):
         if ":" in ln and not ln.startswith("#"):
             a, b = ln.split(":", 1)
             kv[a.strip()] = b.strip()
     if kv.get("kernel_source_sha256_16") != kernel_hash():
-        return None
-    try:
-        return float(kv["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+        return None, None
+
+    def num(key):
+        try:
+            return float(kv[key])
+        except (KeyError, ValueError):
+            return None
+    return num("hbm_bytes_per_launch"), num("sclk_ghz_partial_kernel")
 
 
 def cpu_baseline(w, q, k, v, seconds: float):
@@ -129,14 +133,19 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-small", action="store_true", help="skip the 8K-token GQA workload leg")
+    ap.add_argument("--no-other-order", action="store_true",
+                    help="skip the other ring order (profiling runs: every partial launch is then a ring step)")
     ap.add_argument("--with-1m", action="store_true",
                     help="also time the 1M-token workload (about a minute more: inputs are 4 GiB of Q)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB fp32 copy kernel (counter calibration under rocprofv3 --pmc)")
-    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
+                    help="FETCH_DIR WRITE_DIR [CLOCK_DIR]: HBM traffic (and shader clock) from rocprofv3 --pmc runs")
     args = ap.parse_args(argv)
 
     if args.summarize_pmc:
+        if len(args.summarize_pmc) not in (2, 3):
+            ap.error("--summarize-pmc takes FETCH_DIR WRITE_DIR [CLOCK_DIR]")
         return summarize_pmc(*args.summarize_pmc)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
@@ -198,9 +207,13 @@ def main(argv=None) -> int:
     launches = args.steps * P
     avg_launch_ms = kern_ms_total / launches
     achieved = total_flops * args.steps / (kern_ms_total * 1e-3) / 1e12
-    traffic = read_traffic()
+    traffic, sclk = read_pmc_summary()
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                # the chip does not hold 2.4 GHz under this kernel: the same fraction against the dense
+                # peak at the shader clock measured for it (rocprofv3 GRBM_GUI_ACTIVE, profiles/)
+                "sclk_ghz_measured": sclk,
+                "frac_at_measured_sclk": (round(achieved / (PEAK_BF16_TFLOPS * sclk / 2.4), 4) if sclk else None),
                 "kernel": "partial_bf16_d128_kernel", "launches_per_step": P,
                 "avg_launch_ms": round(avg_launch_ms, 4),
                 "algorithmic_flop_per_launch": total_flops / P}
@@ -230,19 +243,22 @@ def main(argv=None) -> int:
         "device": props.name,
     }
 
-    # Pass-Q ordering of the same prefill (a few steps)
-    other = "pass_q" if args.order == "pass_kv" else "pass_kv"
-    ws2 = torch.empty(cp.ring_prefill_workspace_size(gq, P, other, True), dtype=torch.uint8, device=dev)
-    cp.ring_prefill(gq, gk, gv, P, other, True, out=out, lse=lse, workspace=ws2)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    reps = max(1, args.steps // 2)
-    for _ in range(reps):
+    # the other ring order of the same prefill, as whole ring prefills (all pairs in one launch)
+    if not args.no_other_order:
+        other = "pass_q" if args.order == "pass_kv" else "pass_kv"
+        ws2 = torch.empty(cp.ring_prefill_workspace_size(gq, P, other, True), dtype=torch.uint8, device=dev)
         cp.ring_prefill(gq, gk, gv, P, other, True, out=out, lse=lse, workspace=ws2)
-    torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / reps
-    result[other] = {"ms_per_step": round(dt * 1e3, 3), "TFLOP/s": round(total_flops / dt / 1e12, 2)}
-    del ws2, ws
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        reps = max(1, args.steps // 2)
+        for _ in range(reps):
+            cp.ring_prefill(gq, gk, gv, P, other, True, out=out, lse=lse, workspace=ws2)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / reps
+        result[other] = {"ms_per_step": round(dt * 1e3, 3), "TFLOP/s": round(total_flops / dt / 1e12, 2),
+                         "launch": "ring_prefill: all pairs in one launch, then one merge"}
+        del ws2
+    del ws
 
     def prefill_leg(name: str, reps: int):
         """Median time of whole Pass-KV ring prefills of another workload (2 warm-ups)."""
@@ -339,9 +355,21 @@ def _per_dispatch(rows, counter: str, name_part: str):
     return sum(vals) / len(vals) if vals else None, len(vals)
 
 
-def summarize_pmc(fetch_dir: str, write_dir: str) -> int:
+def _clock_ghz(rows, name_part: str):
+    """Shader clock during a kernel's dispatches: GRBM_GUI_ACTIVE counts busy clocks summed over the
+    8 XCDs (a plain copy kernel reads 8 x ~2.4 GHz on this chip), divided by the dispatch time."""
+    cyc = dur = 0.0
+    for r in rows:
+        if r.get("Counter_Name") == "GRBM_GUI_ACTIVE" and name_part in r.get("Kernel_Name", ""):
+            cyc += float(r["Counter_Value"])
+            dur += float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    return cyc / dur / 8.0 if dur > 0 else None
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, clock_dir: str | None = None) -> int:
     """HBM bytes per partial-kernel launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
-    each scaled by what the same counter reads for the 1 GiB copy kernel."""
+    each scaled by what the same counter reads for the 1 GiB copy kernel; with a third run of
+    GRBM_GUI_ACTIVE, also the shader clock the partial kernel ran at."""
     fr, wr = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
     f_k, nf = _per_dispatch(fr, "FETCH_SIZE", "partial_bf16_d128_kernel")
     w_k, nw = _per_dispatch(wr, "WRITE_SIZE", "partial_bf16_d128_kernel")
@@ -357,7 +385,8 @@ def summarize_pmc(fetch_dir: str, write_dir: str) -> int:
     with open(TRAFFIC_FILE, "w") as f:
         f.write("# HBM traffic of partial_bf16_d128_kernel per launch on the 128K-token workload, Pass-KV\n")
         f.write("# from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs of:\n")
-        f.write("#   python bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-decode --calibrate-copy\n")
+        f.write("#   python bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-decode --no-small --no-other-order --calibrate-copy\n")
+        f.write("# (every partial launch of that run is one Pass-KV ring step)\n")
         f.write("# each counter scaled by its reading for a plain 1 GiB fp32 copy kernel\n")
         f.write(f"kernel_source_sha256_16: {kernel_hash()}\n")
         f.write(f"dispatches: {nf} (FETCH) {nw} (WRITE)\n")
@@ -368,6 +397,12 @@ def summarize_pmc(fetch_dir: str, write_dir: str) -> int:
         f.write(f"fetch_bytes_per_launch: {fetch_b:.0f}\n")
         f.write(f"write_bytes_per_launch: {write_b:.0f}\n")
         f.write(f"hbm_bytes_per_launch: {fetch_b + write_b:.0f}\n")
+        if clock_dir:
+            cr = _pmc_rows(clock_dir)
+            ck, cc = _clock_ghz(cr, "partial_bf16_d128_kernel"), _clock_ghz(cr, "elementwise")
+            f.write("# shader clock from a third run with --pmc GRBM_GUI_ACTIVE: busy clocks / 8 XCDs / dispatch time\n")
+            f.write(f"sclk_ghz_partial_kernel: {ck:.3f}\n")
+            f.write(f"sclk_ghz_copy_kernel: {cc:.3f}\n")
     print(open(TRAFFIC_FILE).read())
     return 0
 
