@@ -229,6 +229,18 @@ def test_workload_128k_both_orders(cp):
         res[order] = cp.ring_prefill(gq, gk, gv, w.n_chunks, order, True)
         torch.cuda.synchronize()
         _sampled_check(cp, w, *res[order], q, k, v, f"{w.name} {order}")
+    # the launch configuration bench.py times: one ring_step launch per step, then ring_merge;
+    # every pair is computed by the same per-block code, so the result is bit-identical
+    banner(w.name, "pass_kv per-step launches")
+    ws = torch.empty(cp.ring_prefill_workspace_size(gq, w.n_chunks, "pass_kv", True), dtype=torch.uint8, device=DEV)
+    o_s = torch.empty_like(res["pass_kv"][0])
+    l_s = torch.empty_like(res["pass_kv"][1])
+    for step in range(w.n_chunks):
+        cp.ring_step(gq, gk, gv, w.n_chunks, step, ws, "pass_kv", True)
+    cp.ring_merge(w.n_chunks, ws, o_s, l_s, "pass_kv", True)
+    torch.cuda.synchronize()
+    assert torch.equal(o_s, res["pass_kv"][0]) and torch.equal(l_s, res["pass_kv"][1])
+    del ws, o_s, l_s
     (okv, lkv), (oq, lq) = res["pass_kv"], res["pass_q"]
     d_o = (okv - oq).abs().max().item()
     d_l = (lkv - lq).abs().max().item()
