@@ -145,6 +145,21 @@ def test_ring_workspace_size_formula():
     assert ring_ws(q, 16, order=5) == 0
 
 
+def test_decode_workspace_size():
+    """Partials per call: n_chunks x sub-splits, the sub-splits doubling while the grid has fewer
+    than 1024 units, each sub-split keeps >= 256 keys, and the merge takes <= 64 partials."""
+    def ws(B, Skv, Hq, Hkv, D, n):
+        q, k = bshd(B, 1, Hq, D), bshd(B, Skv, Hkv, D)
+        return lib.cpattn_splitkv_decode_workspace_size(ctypes.byref(q), ctypes.byref(k), n)
+    up = lambda x: (x + 255) // 256 * 256
+    size = lambda n_part, B, Hq, D: up(n_part * B * Hq * D * 4) + up(n_part * B * Hq * 4)
+    assert ws(128, 32768, 16, 1, 128, 8) == size(8, 128, 16, 128)    # 1024 units already: no sub-split
+    assert ws(1, 32768, 16, 1, 128, 8) == size(64, 1, 16, 128)       # 8 sub-splits: 8 x 8 = 64 partials, the limit
+    assert ws(4, 2048, 16, 1, 128, 4) == size(8, 4, 16, 128)         # 512-key chunks: 2 sub-splits of 256
+    assert ws(2, 96, 8, 2, 64, 3) == size(3, 2, 8, 64)               # chunks too short to split
+    assert ws(2, 100, 8, 2, 64, 3) == 0 and "divide" in err()
+
+
 @no_gpu
 def test_ring_validation():
     r = ctypes.byref
