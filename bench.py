@@ -260,6 +260,27 @@ def main(argv=None) -> int:
         del ws2
     del ws
 
+    def fused_reps(xq, xk, xv, n_chunks: int, xout, xlse, reps: int, label: str):
+        """Median ms of whole fused ring prefills (online merge, one launch; 2 warm-ups)."""
+        for _ in range(2):
+            cp.ring_prefill_fused(xq, xk, xv, n_chunks, True, out=xout, lse=xlse)
+        torch.cuda.synchronize()
+        evf = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        for i in range(reps):
+            evf[i][0].record(stream)
+            cp.ring_prefill_fused(xq, xk, xv, n_chunks, True, out=xout, lse=xlse)
+            evf[i][1].record(stream)
+        torch.cuda.synchronize()
+        msf = sorted(e[0].elapsed_time(e[1]) for e in evf)[reps // 2]
+        log(f"[bench] {label} fused: {msf:.3f} ms")
+        return msf
+
+    if not args.no_other_order:
+        msf = fused_reps(gq, gk, gv, P, out, lse, max(3, args.steps // 2), w.name)
+        result["fused"] = {"ms_per_step": round(msf, 3), "TFLOP/s": round(total_flops / (msf * 1e-3) / 1e12, 2),
+                           "pct_bf16_peak": round(100 * total_flops / (msf * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                           "launch": "ring_prefill_fused: each owner's visible keys in one pass, no merge"}
+
     def prefill_leg(name: str, reps: int):
         """Median time of whole Pass-KV ring prefills of another workload (2 warm-ups)."""
         wx = si.WORKLOADS[name]
@@ -283,10 +304,15 @@ def main(argv=None) -> int:
             log(f"[bench] {wx.name} rep {i + 1}/{reps}: {evx[i][0].elapsed_time(evx[i][1]):.3f} ms")
         msx = sorted(e[0].elapsed_time(e[1]) for e in evx)[reps // 2]
         tf = wx.flops() / (msx * 1e-3) / 1e12
-        del xq, xk, xv, xws, xout, xlse
+        del xws
+        msf = fused_reps(xq, xk, xv, wx.n_chunks, xout, xlse, reps, wx.name)
+        tff = wx.flops() / (msf * 1e-3) / 1e12
+        del xq, xk, xv, xout, xlse
         torch.cuda.empty_cache()
         return {"workload": wx.name, "order": "pass_kv", "ms": round(msx, 4), "TFLOP/s": round(tf, 2),
-                "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2), "flop": wx.flops(), "reps": reps}
+                "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2), "flop": wx.flops(), "reps": reps,
+                "fused": {"ms": round(msf, 4), "TFLOP/s": round(tff, 2),
+                          "pct_bf16_peak": round(100 * tff / PEAK_BF16_TFLOPS, 2)}}
 
     if not args.no_small:
         result["gqa_8k"] = prefill_leg("gqa16_bf16_s8k_p8", max(5, args.steps))

@@ -62,6 +62,7 @@ def _load() -> ctypes.CDLL:
         "cpattn_ring_prefill": ([P, P, P, i32, i32, i32, P, P, vp, sz, vp], i32),
         "cpattn_ring_step": ([P, P, P, i32, i32, i32, i32, vp, sz, vp], i32),
         "cpattn_ring_merge": ([i32, i32, i32, vp, sz, P, P, vp], i32),
+        "cpattn_ring_prefill_fused": ([P, P, P, i32, i32, P, P, vp], i32),
         "cpattn_splitkv_decode_workspace_size": ([P, P, i32], sz),
         "cpattn_splitkv_decode": ([P, P, P, i32, P, P, vp, sz, vp], i32),
         "cpattn_last_error": ([], ctypes.c_char_p),
@@ -174,6 +175,20 @@ def ring_prefill(q, k, v, n_chunks: int, order="pass_kv", causal: bool = True, o
     _check(lib.cpattn_ring_prefill(_ref(dq), _ref(dk), _ref(dv), int(n_chunks), _ORDERS[order], int(bool(causal)),
                                    _ref(do), _ref(dl), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                    _stream(q, stream)))
+    return out, lse
+
+
+def ring_prefill_fused(q, k, v, n_chunks: int, causal: bool = True, out=None, lse=None, want_lse: bool = True,
+                       stream=None):
+    """The ring prefill with the merge done online: one launch, no workspace, fp32 output."""
+    B, S, H, D = q.shape
+    if out is None:
+        out = torch.empty(B, S, H, D, dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty(B, S, H, dtype=torch.float32, device=q.device)
+    dq, dk, dv, do, dl = describe(q), describe(k), describe(v), describe(out), describe(lse, True)
+    _check(lib.cpattn_ring_prefill_fused(_ref(dq), _ref(dk), _ref(dv), int(n_chunks), int(bool(causal)),
+                                         _ref(do), _ref(dl), _stream(q, stream)))
     return out, lse
 
 

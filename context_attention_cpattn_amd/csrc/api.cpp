@@ -111,6 +111,7 @@ cpattn::PartialLaunch base_partial(const cpattn_tensor& q, const cpattn_tensor& 
   a.B = (int32_t)q.B;
   a.Hq = (int32_t)q.H;
   a.G = (int32_t)(q.H / k.H);
+  a.xcd_order = 1;
   return a;
 }
 
@@ -488,6 +489,41 @@ cpattn_status cpattn_ring_prefill(const cpattn_tensor* q, const cpattn_tensor* k
                              "ring prefill launch")) != CPATTN_OK)
     return s;
   return cpattn_ring_merge(n_chunks, order, causal, workspace, workspace_bytes, out, lse, stream);
+}
+
+cpattn_status cpattn_ring_prefill_fused(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                                        int n_chunks, int causal, cpattn_tensor* out, cpattn_tensor* lse,
+                                        void* stream) {
+  cpattn_status s;
+  if ((s = check_ring(q, k, v, n_chunks, CPATTN_PASS_KV, causal)) != CPATTN_OK) return s;
+  if ((s = check_out(out, lse, *q, false, false)) != CPATTN_OK) return s;
+  if (q->S == 0 || q->B == 0) return ok();
+  const int P = n_chunks;
+  const int64_t C = q->S / P;
+  cpattn::PartialLaunch a = base_partial(*q, *k, *v);
+  a.o = static_cast<float*>(out->data);
+  a.o_sb = out->stride_b; a.o_ss = out->stride_s; a.o_sh = out->stride_h;
+  a.o_slot = C * out->stride_s;  // owner i's rows start at row iC of the output
+  if (lse != nullptr) {
+    a.lse = static_cast<float*>(lse->data);
+    a.l_sb = lse->stride_b; a.l_ss = lse->stride_s; a.l_sh = lse->stride_h;
+    a.l_slot = C * lse->stride_s;
+  }
+  a.chunk_len = C;
+  a.Sq = (int32_t)C;
+  a.Sk = (int32_t)q->S;
+  a.causal = causal;
+  // One item per owner: Q chunk i against the keys it sees ([0, (i+1)C) under
+  // the causal mask, all of them otherwise), accumulated in one pass.  The
+  // owners' costs differ up to P-fold, so the grid keeps its launch order
+  // (consecutive workgroups go to different XCDs) with the heaviest owner first.
+  a.xcd_order = 0;
+  a.n_items = 0;
+  for (int i = P - 1; i >= 0; --i)
+    a.items[a.n_items++] = cpattn::Item{i, 0, i, (int32_t)(causal ? (i + 1) * C : q->S)};
+  const hipError_t e = launch_partial(a, q->dtype, (int)q->D, (int)C, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fused ring prefill launch");
+  return ok();
 }
 
 size_t cpattn_splitkv_decode_workspace_size(const cpattn_tensor* q, const cpattn_tensor* k, int n_chunks) {

@@ -7,7 +7,7 @@
 
 namespace cpattn {
 
-constexpr int kMaxItems = 160;  // partial-attention work items per launch (kernel argument ~2 KB)
+constexpr int kMaxItems = 160;  // partial-attention work items per launch (kernel argument ~2.8 KB)
 constexpr int kMaxMerge = 64;   // partials per merge launch (CPATTN_MAX_MERGE)
 
 // One (Q block, K/V block) pair of a launch.  Pointers are derived from the
@@ -17,6 +17,7 @@ struct Item {
   int32_t q_chunk;
   int32_t kv_chunk;
   int32_t slot;
+  int32_t sk;  // keys of this item's K/V block; 0 = the launch's Sk
 };
 
 struct PartialLaunch {
@@ -24,7 +25,7 @@ struct PartialLaunch {
   const void* k;
   const void* v;
   float* o;
-  float* lse;
+  float* lse;     // may be null (no LSE wanted)
   int64_t q_sb, q_ss, q_sh;  // element strides
   int64_t k_sb, k_ss, k_sh;
   int64_t v_sb, v_ss, v_sh;
@@ -36,6 +37,7 @@ struct PartialLaunch {
   int32_t B, Sq, Sk, Hq, G;  // Sq/Sk: rows of one Q/K/V block; G = Hq / Hkv
   int32_t causal;
   int32_t n_items;
+  int32_t xcd_order;  // 1: each XCD takes a contiguous share of the grid; 0: launch order
   Item items[kMaxItems];
 };
 

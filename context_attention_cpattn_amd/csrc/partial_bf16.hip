@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void partial_bf16_kernel(const PartialLaunch a
   // ---- which (item, query tile, batch, head) this workgroup computes
   const int bh = a.B * a.Hq;
   const int per_item = bh * n_qtiles;
-  const int L = xcd_logical_block(blockIdx.x, per_item * a.n_items);
+  const int L = (a.xcd_order ? xcd_logical_block(blockIdx.x, per_item * a.n_items) : (int)blockIdx.x);
   const int item = L / per_item;
   int rem = L - item * per_item;
   const int qt = n_qtiles - 1 - rem / bh;  // later (heavier under the mask) tiles first
@@ -85,6 +85,7 @@ __global__ __launch_bounds__(256) void partial_bf16_kernel(const PartialLaunch a
   const int h = rem - b * a.Hq;
   const int kvh = h / a.G;
   const Item it = a.items[item];
+  const int Sk = it.sk > 0 ? it.sk : a.Sk;  // keys of this item's K/V block
 
   const __bf16* qp = static_cast<const __bf16*>(a.q) + b * a.q_sb + h * a.q_sh +
                      (int64_t)it.q_chunk * a.chunk_len * a.q_ss;
@@ -102,11 +103,11 @@ __global__ __launch_bounds__(256) void partial_bf16_kernel(const PartialLaunch a
   const int row = r0 + l32;       // this lane's query row
 
   // keys [0, n_end) can be visible to some row of this workgroup
-  int n_end = a.Sk;
+  int n_end = Sk;
   if (a.causal) {
     const int64_t last_row = (int64_t)min(m0 + C::BM, a.Sq) - 1;
     const int64_t lim = qpos0 + last_row - kvpos0 + 1;
-    n_end = (int)max<int64_t>(0, min<int64_t>(a.Sk, lim));
+    n_end = (int)max<int64_t>(0, min<int64_t>(Sk, lim));
   }
   const int n_tiles = (n_end + C::BN - 1) / C::BN;
 
@@ -138,12 +139,12 @@ __global__ __launch_bounds__(256) void partial_bf16_kernel(const PartialLaunch a
       for (int i = 0; i < C::KPT; ++i) {
         const int idx = tid + 256 * i;
         const int key = idx / C::DCH, ch = idx % C::DCH;
-        kreg[i] = (n0 + key < a.Sk) ? ld_global16(kp + (int64_t)(n0 + key) * a.k_ss + ch * 8) : (u32x4){};
+        kreg[i] = (n0 + key < Sk) ? ld_global16(kp + (int64_t)(n0 + key) * a.k_ss + ch * 8) : (u32x4){};
       }
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int key = n0 + 4 * vkg + kk;
-        vreg[kk] = (key < a.Sk) ? ld_global16(vp + (int64_t)key * a.v_ss + vch * 8) : (u32x4){};
+        vreg[kk] = (key < Sk) ? ld_global16(vp + (int64_t)key * a.v_ss + vch * 8) : (u32x4){};
       }
     };
     auto store_tile = [&](int stage) {
@@ -197,11 +198,11 @@ __global__ __launch_bounds__(256) void partial_bf16_kernel(const PartialLaunch a
         }
 
         // ---- mask (only tiles that straddle the diagonal or the block end)
-        const bool full = (n0 + C::BN <= a.Sk) && (!a.causal || kvpos0 + n0 + C::BN - 1 <= qpos0 + r0);
+        const bool full = (n0 + C::BN <= Sk) && (!a.causal || kvpos0 + n0 + C::BN - 1 <= qpos0 + r0);
         if (!full) {
           // visibility is monotone in the key, so this row sees exactly the
           // tile-local keys [0, lim)
-          int64_t lim64 = (int64_t)a.Sk - n0;
+          int64_t lim64 = (int64_t)Sk - n0;
           if (a.causal) lim64 = min<int64_t>(lim64, qpos0 + row - kvpos0 - n0 + 1);
           const int lim = (int)max<int64_t>(0, min<int64_t>(lim64, C::BN));
 #pragma unroll
@@ -289,7 +290,7 @@ __global__ __launch_bounds__(256) void partial_bf16_kernel(const PartialLaunch a
         *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * i4 + 4 * g) = v4;
       }
     }
-    if (g == 0) lp[(int64_t)row * a.l_ss] = (l_tot > 0.f) ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
+    if (g == 0 && a.lse != nullptr) lp[(int64_t)row * a.l_ss] = (l_tot > 0.f) ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
   }
 }
 
@@ -377,7 +378,7 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
 
   const int bh = a.B * a.Hq;
   const int per_item = bh * n_qtiles;
-  const int L = xcd_logical_block(blockIdx.x, per_item * a.n_items);
+  const int L = (a.xcd_order ? xcd_logical_block(blockIdx.x, per_item * a.n_items) : (int)blockIdx.x);
   const int item = L / per_item;
   int rem = L - item * per_item;
   const int qt = n_qtiles - 1 - rem / bh;
@@ -386,6 +387,7 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
   const int h = rem - b * a.Hq;
   const int kvh = h / a.G;
   const Item it = a.items[item];
+  const int Sk = it.sk > 0 ? it.sk : a.Sk;  // keys of this item's K/V block
 
   const __bf16* qp = static_cast<const __bf16*>(a.q) + b * a.q_sb + h * a.q_sh +
                      (int64_t)it.q_chunk * a.chunk_len * a.q_ss;
@@ -403,8 +405,8 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
   const int r0 = m0 + wave * 32;
   const int row = r0 + l32;
 
-  int n_end = a.Sk;
-  if (a.causal) n_end = max(0, min(a.Sk, min(m0 + BM, a.Sq) - dpos));
+  int n_end = Sk;
+  if (a.causal) n_end = max(0, min(Sk, min(m0 + BM, a.Sq) - dpos));
   const int n_tiles = (n_end + BN - 1) / BN;
 
   f32x16 o[4];
@@ -454,7 +456,7 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
     auto fetch = [&](int stage) {
       const uint32_t dst = lbase + stage * STAGE;
       if (fetcher) {
-        if ((n_fetched + 1) * BN <= a.Sk) {
+        if ((n_fetched + 1) * BN <= Sk) {
 #pragma unroll
           for (int i = 0; i < FL; ++i) {
             gload_lds16(kf[i], dst + i * FW * 64 * 16);
@@ -465,7 +467,7 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
           // masked to -inf, so their p is exactly 0
 #pragma unroll
           for (int i = 0; i < FL; ++i) {
-            const int over = max(0, n_fetched * BN + fkey[i] - (a.Sk - 1));
+            const int over = max(0, n_fetched * BN + fkey[i] - (Sk - 1));
             gload_lds16(kf[i] - over * a.k_ss, dst + i * FW * 64 * 16);
             gload_lds16(vf[i] - over * a.v_ss, dst + i * FW * 64 * 16 + TBYTES);
           }
@@ -481,8 +483,8 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
 
     auto mask_tile = [&](f32x16 (&sc)[2], int t) {
       const int n0 = t * BN;
-      if (n0 + BN > a.Sk || (a.causal && dpos + n0 + BN - 1 > r0)) {
-        int lim = a.Sk - n0;
+      if (n0 + BN > Sk || (a.causal && dpos + n0 + BN - 1 > r0)) {
+        int lim = Sk - n0;
         if (a.causal) lim = min(lim, row - dpos - n0 + 1);
         mask_block(sc, max(0, min(lim, BN)), g);
       }
@@ -664,7 +666,7 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
                           o[db][4 * i4 + 3] * inv};
         *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * i4 + 4 * g) = v4;
       }
-    if (g == 0) lp[(int64_t)row * a.l_ss] = (l_tot > 0.f) ? (m + fast_log2(l_tot)) * kLn2 : kNegInf;
+    if (g == 0 && a.lse != nullptr) lp[(int64_t)row * a.l_ss] = (l_tot > 0.f) ? (m + fast_log2(l_tot)) * kLn2 : kNegInf;
   }
 }
 

@@ -28,7 +28,7 @@ __global__ __launch_bounds__(256) void partial_f32_kernel(const PartialLaunch a,
   const int part = tid % T;
   const int bh = a.B * a.Hq;
   const int per_item = bh * n_qtiles;
-  const int L = xcd_logical_block(blockIdx.x, per_item * a.n_items);
+  const int L = (a.xcd_order ? xcd_logical_block(blockIdx.x, per_item * a.n_items) : (int)blockIdx.x);
   const int item = L / per_item;
   int rem = L - item * per_item;
   const int qt = n_qtiles - 1 - rem / bh;
@@ -37,6 +37,7 @@ __global__ __launch_bounds__(256) void partial_f32_kernel(const PartialLaunch a,
   const int h = rem - b * a.Hq;
   const int kvh = h / a.G;
   const Item it = a.items[item];
+  const int Sk = it.sk > 0 ? it.sk : a.Sk;  // keys of this item's K/V block
 
   const float* qp = static_cast<const float*>(a.q) + b * a.q_sb + h * a.q_sh +
                     (int64_t)it.q_chunk * a.chunk_len * a.q_ss;
@@ -54,10 +55,10 @@ __global__ __launch_bounds__(256) void partial_f32_kernel(const PartialLaunch a,
   const bool row_ok = row < a.Sq;
   const int64_t qpos = qpos0 + row;
 
-  int n_end = a.Sk;
+  int n_end = Sk;
   if (a.causal) {
     const int64_t last_row = (int64_t)min(m0 + ROWS, a.Sq) - 1;
-    n_end = (int)max<int64_t>(0, min<int64_t>(a.Sk, qpos0 + last_row - kvpos0 + 1));
+    n_end = (int)max<int64_t>(0, min<int64_t>(Sk, qpos0 + last_row - kvpos0 + 1));
   }
 
   float q[32], o[32];
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(256) void partial_f32_kernel(const PartialLaunch a,
     // cooperative tile load: BN*D floats of K and of V, 16 bytes per thread per pass
     for (int idx = tid; idx < BN * D / 4; idx += 256) {
       const int key = (idx * 4) / D, d = (idx * 4) % D;
-      const bool ok = n0 + key < a.Sk;
+      const bool ok = n0 + key < Sk;
       *reinterpret_cast<f32x4*>(ks + key * D + d) =
           ok ? *reinterpret_cast<const f32x4*>(kp + (int64_t)(n0 + key) * a.k_ss + d) : (f32x4){};
       *reinterpret_cast<f32x4*>(vs + key * D + d) =
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(256) void partial_f32_kernel(const PartialLaunch a,
 #pragma unroll
     for (int x = 0; x < 32; x += 4)
       *reinterpret_cast<f32x4*>(orow + x) = (f32x4){o[x] * inv, o[x + 1] * inv, o[x + 2] * inv, o[x + 3] * inv};
-    if (part == 0) lp[(int64_t)row * a.l_ss] = (l > 0.f) ? (m + fast_log2(l)) * kLn2 : kNegInf;
+    if (part == 0 && a.lse != nullptr) lp[(int64_t)row * a.l_ss] = (l > 0.f) ? (m + fast_log2(l)) * kLn2 : kNegInf;
   }
 }
 

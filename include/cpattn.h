@@ -179,6 +179,26 @@ cpattn_status cpattn_ring_merge(int n_chunks, cpattn_order order, int causal,
                                 cpattn_tensor* out, cpattn_tensor* lse, void* stream);
 
 /*
+ * cpattn_ring_prefill_fused - the ring prefill with the merge done online.
+ *
+ * Every Q chunk's partials are accumulated into one running (O, LSE) as the
+ * K/V chunks reach it, instead of being stored and merged afterwards (the
+ * pieces gathered around the ring accumulated into the full result: "The
+ * communication bottleneck across all three axes", soumitrasaha.com reader
+ * notes).  On one device the owner of Q chunk i sees the keys [0, (i+1)C)
+ * (all of them without the causal mask) in one pass, in position order;
+ * any order of the same keys is exact up to rounding, so the result equals
+ * cpattn_ring_prefill's within rounding.  No workspace, one launch.
+ *   q, k, v  as for cpattn_ring_prefill
+ *   out      [B, S, Hq, D] F32
+ *   lse      [B, S, Hq] F32, or NULL to skip
+ * Errors as for cpattn_ring_prefill (out must be F32).
+ */
+cpattn_status cpattn_ring_prefill_fused(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                                        int n_chunks, int causal, cpattn_tensor* out, cpattn_tensor* lse,
+                                        void* stream);
+
+/*
  * cpattn_splitkv_decode_workspace_size - bytes of workspace
  * cpattn_splitkv_decode needs (0 if the arguments are invalid).
  */

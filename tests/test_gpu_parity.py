@@ -175,6 +175,33 @@ def test_ring_merge_follows_arrival_order(cp, P, order, causal):
         assert torch.equal(lm, l[:, i * C:(i + 1) * C]), f"owner {i}: LSE differs"
 
 
+@pytest.mark.parametrize("P,causal,Hkv,D", [(1, True, 1, 128), (4, True, 2, 128), (5, False, 1, 128), (3, True, 1, 64),
+                                           (6, True, 4, 64)])
+def test_ring_prefill_fused(cp, P, causal, Hkv, D):
+    S = 120 * P  # ragged query tiles inside every chunk
+    q = draw(71 + P, (2, S, 4, D), torch.bfloat16, 0)
+    k = draw(71 + P, (2, S, Hkv, D), torch.bfloat16, 1)
+    v = draw(71 + P, (2, S, Hkv, D), torch.bfloat16, 2)
+    o_ref, l_ref = oracle.ring_attention(q, k, v, P, "pass_kv", causal)
+    banner("ring fused", P, causal, Hkv, D)
+    o, l = cp.ring_prefill_fused(q.to(DEV), k.to(DEV), v.to(DEV), P, causal)
+    torch.cuda.synchronize()
+    compare(o, l, o_ref, l_ref, BF16_TOL, f"ring fused P={P} causal={causal} Hkv={Hkv} D={D}")
+
+
+def test_ring_prefill_fused_f32_and_no_lse(cp):
+    S, P = 300, 3
+    q = draw(81, (1, S, 2, 64), torch.float32, 0)
+    k = draw(81, (1, S, 1, 64), torch.float32, 1)
+    v = draw(81, (1, S, 1, 64), torch.float32, 2)
+    o_ref, _ = oracle.ring_attention(q, k, v, P, "pass_kv", True)
+    banner("ring fused f32")
+    o, l = cp.ring_prefill_fused(q.to(DEV), k.to(DEV), v.to(DEV), P, True, want_lse=False)
+    torch.cuda.synchronize()
+    assert l is None
+    assert (o.double().cpu() - o_ref).abs().max().item() < 1e-4
+
+
 def test_workload_gqa_8k(cp):
     w = si.WORKLOADS["gqa16_bf16_s8k_p8"]
     q, k, v = si.make_qkv(w)
@@ -184,6 +211,10 @@ def test_workload_gqa_8k(cp):
     o, l = cp.ring_prefill(q.to(DEV), k.to(DEV), v.to(DEV), w.n_chunks, "pass_kv", True)
     torch.cuda.synchronize()
     compare(o, l, o_ref, l_ref, BF16_TOL, w.name)
+    banner(w.name, "ring_prefill_fused", w.n_chunks)
+    o, l = cp.ring_prefill_fused(q.to(DEV), k.to(DEV), v.to(DEV), w.n_chunks, True)
+    torch.cuda.synchronize()
+    compare(o, l, o_ref, l_ref, BF16_TOL, w.name + " fused")
 
 
 def test_workload_decode_32k(cp):
@@ -246,6 +277,22 @@ def test_workload_128k_both_orders(cp):
     d_l = (lkv - lq).abs().max().item()
     print(f"[parity] {w.name}: pass_kv vs pass_q max|dO|={d_o:.3e} max|dLSE|={d_l:.3e}", flush=True)
     assert d_o <= 1e-5 and d_l <= 1e-5
+    del oq, lq
+    # the fused ring prefill (online merge, one launch): the same sampled rows against the oracle,
+    # and every row against the per-pair path.  The two round P to bf16 against different running
+    # maxima, so they differ by bf16 rounding of P, not by fp32 reordering alone: the bar between
+    # them is the bf16 tolerance each already meets against the oracle.
+    banner(w.name, "ring_prefill_fused", w.n_chunks)
+    of, lf = cp.ring_prefill_fused(gq, gk, gv, w.n_chunks, True)
+    torch.cuda.synchronize()
+    _sampled_check(cp, w, of, lf, q, k, v, f"{w.name} fused")
+    d = (okv - of).abs_()
+    d_o, m_o = d.max().item(), d.mean().item()
+    del d
+    d_l = (lkv - lf).abs().max().item()
+    print(f"[parity] {w.name}: fused vs pass_kv max|dO|={d_o:.3e} mean|dO|={m_o:.3e} max|dLSE|={d_l:.3e}",
+          flush=True)
+    assert d_o <= BF16_TOL.max_abs and m_o <= BF16_TOL.mean_abs and d_l <= BF16_TOL.lse_abs
     # properties over every row: finite output, LSE within its possible range
     assert torch.isfinite(okv).all() and torch.isfinite(lkv).all()
 
