@@ -137,3 +137,26 @@ def test_decode_shapes(cp, B, Skv, G, Hkv, n, D):
     o, l = cp.splitkv_decode(q.to(DEV), k.to(DEV), v.to(DEV), n)
     torch.cuda.synchronize()
     compare(o, l, o_ref, l_ref, BF16_TOL, f"decode B{B} Skv{Skv} G{G} Hkv{Hkv} n{n} D{D}")
+
+
+def test_decode_after_prefill_matches_last_row(cp):
+    """The prefill's last token decoded against the same K/V, split into the prefill's CP
+    chunks: split-KV decode, the one-row partial and both prefill paths compute one row."""
+    S, P, B = 4096, 8, 2
+    q, k, v = qkv(21, S, 16, 1, 128, B=B)
+    qlast = q[:, S - 1:S]  # strided view: row S-1 of each sequence
+    o_ref, l_ref = oracle.attention_rows(qlast.cpu(), k.cpu(), v.cpu(), [S - 1], causal=True)
+    banner("prefill then decode", S, P)
+    o, l = cp.ring_prefill(q, k, v, P, "pass_kv", True)
+    of, lf = cp.ring_prefill_fused(q, k, v, P, True)
+    od, ld = cp.splitkv_decode(qlast, k, v, P)
+    op, lp = cp.partial(qlast, k, v, S - 1, 0, True)
+    torch.cuda.synchronize()
+    rows = {"ring_prefill": (o[:, S - 1:S], l[:, S - 1:S]), "fused": (of[:, S - 1:S], lf[:, S - 1:S]),
+            "splitkv_decode": (od, ld), "one-row partial": (op, lp)}
+    for name, (x, y) in rows.items():
+        compare(x, y, o_ref, l_ref, BF16_TOL, f"last row by {name}")
+    for name, (x, y) in rows.items():
+        d_o = (x - od).abs().max().item()
+        d_l = (y - ld).abs().max().item()
+        assert d_o <= BF16_TOL.max_abs and d_l <= BF16_TOL.lse_abs, (name, d_o, d_l)
