@@ -318,8 +318,11 @@ __global__ __launch_bounds__(256) void partial_bf16_kernel(const PartialLaunch a
 //      evaluates, packs and sums key block 1 of P(t);
 //   B: O^T += V(t)^T P(t)^T on the matrix cores, while the vector unit does
 //      key block 0 of P(t+1).
-// Each MFMA is followed by its slice of the vector work (one probability);
-// a scheduling fence after every slice and empty asm "uses" of its results
+// Each MFMA is followed by its slice of the vector work (one probability),
+// skewed over three slots: slot j takes the exponential of score j, the
+// exponent argument of score j+1 and the row-sum add and bf16 pack of score
+// j-1, so no instruction of a slot waits on another of the same slot.  A
+// scheduling fence after every slice and empty asm "uses" of its results
 // keep the compiler from regrouping them.  Waves in phase A outrank waves in
 // phase B, so the wave of a SIMD pair that falls behind catches up.
 //
@@ -585,24 +588,36 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
       f32x16 x[2] = {(f32x16){}, (f32x16){}};
 #pragma unroll
       for (int j = 0; j < KLA; ++j) kop[j] = ld_lds16(nxt + koff[j >> 1] + (j & 1) * 8192);
+      float pe = 0.f, pp = 0.f;
+      float xa = fmaf(s1[0], SCALE_LOG2, -mref);
+      pin(xa);
       __builtin_amdgcn_sched_barrier(0);
-      float pe = 0.f;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         if (j + KLA < 16) kop[j + KLA] = ld_lds16(nxt + koff[(j + KLA) >> 1] + ((j + KLA) & 1) * 8192);
         if (j >= 16 - VLA) read_v(j - (16 - VLA));
         x[j & 1] = mfma32(as_bf16x8(kop[j]), qf[j >> 1], x[j & 1]);
-        const float pv = prob(s1[j]);
-        if (j & 1) {
-          pw[8 + (j >> 1)] = pack_bf16(pe, pv);
-          pin(pw[8 + (j >> 1)]);
-        } else {
-          pe = pv;
-          pin(pe);
+        // slot j: exponent of score j, argument of score j+1, sum and pack of score j-1
+        const float pv = fast_exp2(xa);
+        if (j < 15) xa = fmaf(s1[j + 1], SCALE_LOG2, -mref);
+        if (j > 0) {
+          lt += pp;
+          if ((j - 1) & 1) {
+            pw[8 + ((j - 1) >> 1)] = pack_bf16(pe, pp);
+            pin(pw[8 + ((j - 1) >> 1)]);
+          } else {
+            pe = pp;
+            pin(pe);
+          }
         }
+        pp = pv;
+        pin(pp);
+        pin(xa);
         pin(lt);
         __builtin_amdgcn_sched_barrier(0);
       }
+      lt += pp;
+      pw[15] = pack_bf16(pe, pp);
       sn[0] = x[0];
       sn[1] = x[1];
       mask_tile(sn, t + 1);
@@ -620,8 +635,10 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
         for (int db = 0; db < 4; ++db) o[db] *= alpha;
         need = false;
       }
-      __builtin_amdgcn_sched_barrier(0);
       uint32_t pn[8];
+      xa = fmaf(sn[0][0], SCALE_LOG2, -mref);
+      pin(xa);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
         if (jj + VLA < 16) read_v(jj + VLA);
@@ -629,17 +646,26 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
         const u32x4 av = {vlo[jj][0], vlo[jj][1], vhi[jj][0], vhi[jj][1]};
         const u32x4 bp = {pw[4 * u], pw[4 * u + 1], pw[4 * u + 2], pw[4 * u + 3]};
         o[db] = mfma32(as_bf16x8(av), as_bf16x8(bp), o[db]);
-        const float pv = prob(sn[0][jj]);
-        if (jj & 1) {
-          pn[jj >> 1] = pack_bf16(pe, pv);
-          pin(pn[jj >> 1]);
-        } else {
-          pe = pv;
-          pin(pe);
+        const float pv = fast_exp2(xa);
+        if (jj < 15) xa = fmaf(sn[0][jj + 1], SCALE_LOG2, -mref);
+        if (jj > 0) {
+          lt += pp;
+          if ((jj - 1) & 1) {
+            pn[(jj - 1) >> 1] = pack_bf16(pe, pp);
+            pin(pn[(jj - 1) >> 1]);
+          } else {
+            pe = pp;
+            pin(pe);
+          }
         }
+        pp = pv;
+        pin(pp);
+        pin(xa);
         pin(lt);
         __builtin_amdgcn_sched_barrier(0);
       }
+      lt += pp;
+      pn[7] = pack_bf16(pe, pp);
 #pragma unroll
       for (int w = 0; w < 8; ++w) pw[w] = pn[w];
       STAMP(wave, t, 2, L);
