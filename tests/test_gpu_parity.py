@@ -137,7 +137,8 @@ def test_workload_tiny_bf16_copy(cp):
 
 
 @pytest.mark.parametrize("P,order,causal", [(1, "pass_kv", True), (3, "pass_q", True), (5, "pass_kv", False),
-                                            (6, "pass_q", False), (8, "pass_kv", True)])
+                                            (6, "pass_q", False), (8, "pass_kv", True),
+                                            (64, "pass_kv", True), (64, "pass_q", False)])  # 64: the chunk limit
 def test_ring_small_orders(cp, P, order, causal):
     S = 120 * P  # 120-token chunks: one ragged query tile per chunk
     q = draw(31 + P, (1, S, 4, 128), torch.bfloat16, 0)
@@ -176,13 +177,13 @@ def test_ring_merge_follows_arrival_order(cp, P, order, causal):
 
 
 @pytest.mark.parametrize("P,causal,Hkv,D", [(1, True, 1, 128), (4, True, 2, 128), (5, False, 1, 128), (3, True, 1, 64),
-                                           (6, True, 4, 64)])
+                                           (6, True, 4, 64), (64, True, 1, 128), (64, False, 2, 64)])
 def test_ring_prefill_fused(cp, P, causal, Hkv, D):
     S = 120 * P  # ragged query tiles inside every chunk
     q = draw(71 + P, (2, S, 4, D), torch.bfloat16, 0)
     k = draw(71 + P, (2, S, Hkv, D), torch.bfloat16, 1)
     v = draw(71 + P, (2, S, Hkv, D), torch.bfloat16, 2)
-    o_ref, l_ref = oracle.ring_attention(q, k, v, P, "pass_kv", causal)
+    o_ref, l_ref = oracle.full_attention(q, k, v, causal)
     banner("ring fused", P, causal, Hkv, D)
     o, l = cp.ring_prefill_fused(q.to(DEV), k.to(DEV), v.to(DEV), P, causal)
     torch.cuda.synchronize()
