@@ -118,7 +118,14 @@ def cpu_baseline(w, q, k, v, seconds: float):
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu)
+    except OSError:
+        pass
     return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": torch.get_num_threads(), "kind": "oracle",
+            "cpu": cpu, "seconds": round(dt, 2),
             "sample": f"{n} query rows x {w.Hq} heads of {w.name} at full causal context (fp64, torch CPU), "
                       f"{done_flops:.3e} FLOP in {dt:.1f} s"}
 
