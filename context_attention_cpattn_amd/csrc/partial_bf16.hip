@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void partial_bf16_kernel(const PartialLaunch a
   const __bf16* vp = static_cast<const __bf16*>(a.v) + b * a.v_sb + kvh * a.v_sh +
                      (int64_t)it.kv_chunk * a.chunk_len * a.v_ss;
   float* op = a.o + it.slot * a.o_slot + b * a.o_sb + h * a.o_sh;
-  float* lp = a.lse + it.slot * a.l_slot + b * a.l_sb + h * a.l_sh;
+  float* lp = a.lse != nullptr ? a.lse + it.slot * a.l_slot + b * a.l_sb + h * a.l_sh : nullptr;  // LSE optional
   const int64_t qpos0 = a.q_pos0 + (int64_t)it.q_chunk * a.chunk_len;
   const int64_t kvpos0 = a.kv_pos0 + (int64_t)it.kv_chunk * a.chunk_len;
 
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(256) void partial_bf16_kernel(const PartialLaunch a
         *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * i4 + 4 * g) = v4;
       }
     }
-    if (g == 0 && a.lse != nullptr) lp[(int64_t)row * a.l_ss] = (l_tot > 0.f) ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
+    if (g == 0 && lp != nullptr) lp[(int64_t)row * a.l_ss] = (l_tot > 0.f) ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
   }
 }
 
@@ -399,7 +399,7 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
   const __bf16* vp = static_cast<const __bf16*>(a.v) + b * a.v_sb + kvh * a.v_sh +
                      (int64_t)it.kv_chunk * a.chunk_len * a.v_ss;
   float* op = a.o + it.slot * a.o_slot + b * a.o_sb + h * a.o_sh;
-  float* lp = a.lse + it.slot * a.l_slot + b * a.l_sb + h * a.l_sh;
+  float* lp = a.lse != nullptr ? a.lse + it.slot * a.l_slot + b * a.l_sb + h * a.l_sh : nullptr;  // LSE optional
   const int64_t qpos0 = a.q_pos0 + (int64_t)it.q_chunk * a.chunk_len;
   const int64_t kvpos0 = a.kv_pos0 + (int64_t)it.kv_chunk * a.chunk_len;
 
@@ -692,7 +692,7 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
                           o[db][4 * i4 + 3] * inv};
         *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * i4 + 4 * g) = v4;
       }
-    if (g == 0 && a.lse != nullptr) lp[(int64_t)row * a.l_ss] = (l_tot > 0.f) ? (m + fast_log2(l_tot)) * kLn2 : kNegInf;
+    if (g == 0 && lp != nullptr) lp[(int64_t)row * a.l_ss] = (l_tot > 0.f) ? (m + fast_log2(l_tot)) * kLn2 : kNegInf;
   }
 }
 

@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void partial_f32_kernel(const PartialLaunch a,
   const float* vp = static_cast<const float*>(a.v) + b * a.v_sb + kvh * a.v_sh +
                     (int64_t)it.kv_chunk * a.chunk_len * a.v_ss;
   float* op = a.o + it.slot * a.o_slot + b * a.o_sb + h * a.o_sh;
-  float* lp = a.lse + it.slot * a.l_slot + b * a.l_sb + h * a.l_sh;
+  float* lp = a.lse != nullptr ? a.lse + it.slot * a.l_slot + b * a.l_sb + h * a.l_sh : nullptr;  // LSE optional
   const int64_t qpos0 = a.q_pos0 + (int64_t)it.q_chunk * a.chunk_len;
   const int64_t kvpos0 = a.kv_pos0 + (int64_t)it.kv_chunk * a.chunk_len;
 
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256) void partial_f32_kernel(const PartialLaunch a,
 #pragma unroll
     for (int x = 0; x < 32; x += 4)
       *reinterpret_cast<f32x4*>(orow + x) = (f32x4){o[x] * inv, o[x + 1] * inv, o[x + 2] * inv, o[x + 3] * inv};
-    if (part == 0 && a.lse != nullptr) lp[(int64_t)row * a.l_ss] = (l > 0.f) ? (m + fast_log2(l)) * kLn2 : kNegInf;
+    if (part == 0 && lp != nullptr) lp[(int64_t)row * a.l_ss] = (l > 0.f) ? (m + fast_log2(l)) * kLn2 : kNegInf;
   }
 }
 
