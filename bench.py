@@ -220,6 +220,9 @@ def main(argv=None) -> int:
                 # the chip does not hold 2.4 GHz under this kernel: the same fraction against the dense
                 # peak at the shader clock measured for it (rocprofv3 GRBM_GUI_ACTIVE, profiles/)
                 "sclk_ghz_measured": sclk,
+                "sclk_source": ("rocprofv3 GRBM_GUI_ACTIVE run of this kernel source on another box "
+                                "(profiles/partial_bf16_prefill_s128k_p16_traffic.txt); boxes differ by ~5%"
+                                if sclk else None),
                 "frac_at_measured_sclk": (round(achieved / (PEAK_BF16_TFLOPS * sclk / 2.4), 4) if sclk else None),
                 "kernel": "partial_bf16_d128_kernel", "launches_per_step": P,
                 "avg_launch_ms": round(avg_launch_ms, 4),
