@@ -18,7 +18,7 @@ prefills, the merge kernel's bandwidth, and the fp64 CPU oracle timed on a
 bounded sample.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1]
-  python bench.py --summarize-pmc FETCH_DIR WRITE_DIR   # traffic summary from two rocprofv3 --pmc runs
+  python bench.py --summarize-pmc FETCH_DIR WRITE_DIR [CLOCK_DIR [SQ_DIR]]   # summary of rocprofv3 --pmc runs
 """
 from __future__ import annotations
 
@@ -147,12 +147,13 @@ def main(argv=None) -> int:
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB fp32 copy kernel (counter calibration under rocprofv3 --pmc)")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
-                    help="FETCH_DIR WRITE_DIR [CLOCK_DIR]: HBM traffic (and shader clock) from rocprofv3 --pmc runs")
+                    help="FETCH_DIR WRITE_DIR [CLOCK_DIR [SQ_DIR]]: HBM traffic (shader clock, MFMA busy "
+                         "fraction) from rocprofv3 --pmc runs")
     args = ap.parse_args(argv)
 
     if args.summarize_pmc:
-        if len(args.summarize_pmc) not in (2, 3):
-            ap.error("--summarize-pmc takes FETCH_DIR WRITE_DIR [CLOCK_DIR]")
+        if len(args.summarize_pmc) not in (2, 3, 4):
+            ap.error("--summarize-pmc takes FETCH_DIR WRITE_DIR [CLOCK_DIR [SQ_DIR]]")
         return summarize_pmc(*args.summarize_pmc)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
@@ -402,10 +403,11 @@ def _clock_ghz(rows, name_part: str):
     return cyc / dur / 8.0 if dur > 0 else None
 
 
-def summarize_pmc(fetch_dir: str, write_dir: str, clock_dir: str | None = None) -> int:
+def summarize_pmc(fetch_dir: str, write_dir: str, clock_dir: str | None = None, sq_dir: str | None = None) -> int:
     """HBM bytes per partial-kernel launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
     each scaled by what the same counter reads for the 1 GiB copy kernel; with a third run of
-    GRBM_GUI_ACTIVE, also the shader clock the partial kernel ran at."""
+    GRBM_GUI_ACTIVE, also the shader clock the partial kernel ran at; with a fourth run of
+    GRBM_GUI_ACTIVE and SQ counters, the MFMA busy fraction and the instruction mix."""
     fr, wr = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
     f_k, nf = _per_dispatch(fr, "FETCH_SIZE", "partial_bf16_d128_kernel")
     w_k, nw = _per_dispatch(wr, "WRITE_SIZE", "partial_bf16_d128_kernel")
@@ -439,6 +441,26 @@ def summarize_pmc(fetch_dir: str, write_dir: str, clock_dir: str | None = None) 
             f.write("# shader clock from a third run with --pmc GRBM_GUI_ACTIVE: busy clocks / 8 XCDs / dispatch time\n")
             f.write(f"sclk_ghz_partial_kernel: {ck:.3f}\n")
             f.write(f"sclk_ghz_copy_kernel: {cc:.3f}\n")
+        if sq_dir:
+            sr = _pmc_rows(sq_dir)
+            k = "partial_bf16_d128_kernel"
+            tot = {}
+            for name in ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_MFMA",
+                         "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE"):
+                tot[name], _ = _per_dispatch(sr, name, k)
+            if None in tot.values():
+                raise SystemExit("missing SQ counters for the partial kernel")
+            simds = 4 * 256
+            f.write("# fourth run: --pmc GRBM_GUI_ACTIVE and SQ counters, averages per partial-kernel dispatch\n")
+            for name, val in tot.items():
+                f.write(f"{name.lower()}: {val:.0f}\n")
+            f.write("# MFMA busy cycles per SIMD over the busy cycles of one XCD (GRBM_GUI_ACTIVE / 8)\n")
+            f.write(f"mfma_busy_fraction: {tot['SQ_VALU_MFMA_BUSY_CYCLES'] / (tot['GRBM_GUI_ACTIVE'] / 8.0 * simds):.3f}\n")
+            f.write(f"valu_insts_per_mfma: {tot['SQ_INSTS_VALU'] / tot['SQ_INSTS_MFMA']:.2f}  (SQ_INSTS_VALU counts MFMAs too)\n")
+            f.write(f"lds_insts_per_mfma: {tot['SQ_INSTS_LDS'] / tot['SQ_INSTS_MFMA']:.2f}\n")
+            f.write(f"salu_insts_per_mfma: {tot['SQ_INSTS_SALU'] / tot['SQ_INSTS_MFMA']:.2f}\n")
+            f.write(f"lds_bank_conflict_cycles_per_lds_active_cycle: "
+                    f"{tot['SQ_LDS_BANK_CONFLICT'] / tot['SQ_LDS_IDX_ACTIVE']:.3f}\n")
     print(open(TRAFFIC_FILE).read())
     return 0
 
