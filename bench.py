@@ -75,24 +75,24 @@ def ring_step_flops(w, order: str):
 
 
 def read_pmc_summary():
-    """(HBM bytes per launch, shader clock GHz) of the partial kernel from the committed pmc
-    summary, each None if absent or if the kernel source changed since it was taken."""
+    """(HBM bytes per launch, shader clock GHz, MFMA busy fraction) of the partial kernel from the
+    committed pmc summary, each None if absent or if the kernel source changed since it was taken."""
     if not os.path.exists(TRAFFIC_FILE):
-        return None, None
+        return None, None, None
     kv = {}
     for ln in open(TRAFFIC_FILE):
         if ":" in ln and not ln.startswith("#"):
             a, b = ln.split(":", 1)
             kv[a.strip()] = b.strip()
     if kv.get("kernel_source_sha256_16") != kernel_hash():
-        return None, None
+        return None, None, None
 
     def num(key):
         try:
             return float(kv[key])
         except (KeyError, ValueError):
             return None
-    return num("hbm_bytes_per_launch"), num("sclk_ghz_partial_kernel")
+    return num("hbm_bytes_per_launch"), num("sclk_ghz_partial_kernel"), num("mfma_busy_fraction")
 
 
 def cpu_baseline(w, q, k, v, seconds: float):
@@ -215,7 +215,7 @@ def main(argv=None) -> int:
     launches = args.steps * P
     avg_launch_ms = kern_ms_total / launches
     achieved = total_flops * args.steps / (kern_ms_total * 1e-3) / 1e12
-    traffic, sclk = read_pmc_summary()
+    traffic, sclk, mfma_busy = read_pmc_summary()
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 # the chip does not hold 2.4 GHz under this kernel: the same fraction against the dense
@@ -225,6 +225,7 @@ def main(argv=None) -> int:
                                 "(profiles/partial_bf16_prefill_s128k_p16_traffic.txt); boxes differ by ~5%"
                                 if sclk else None),
                 "frac_at_measured_sclk": (round(achieved / (PEAK_BF16_TFLOPS * sclk / 2.4), 4) if sclk else None),
+                "mfma_busy_fraction_profiled": mfma_busy,
                 "kernel": "partial_bf16_d128_kernel", "launches_per_step": P,
                 "avg_launch_ms": round(avg_launch_ms, 4),
                 "algorithmic_flop_per_launch": total_flops / P}
