@@ -18,7 +18,7 @@ prefills, the merge kernel's bandwidth, and the fp64 CPU oracle timed on a
 bounded sample.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1]
-  python bench.py --summarize-pmc FETCH_DIR WRITE_DIR [CLOCK_DIR [SQ_DIR]]   # summary of rocprofv3 --pmc runs
+  python bench.py --summarize-pmc FETCH_DIR WRITE_DIR [CLOCK_DIR [SQ_DIR [RDREQ_DIR]]]   # rocprofv3 --pmc summary
 """
 from __future__ import annotations
 
@@ -147,13 +147,13 @@ def main(argv=None) -> int:
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB fp32 copy kernel (counter calibration under rocprofv3 --pmc)")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
-                    help="FETCH_DIR WRITE_DIR [CLOCK_DIR [SQ_DIR]]: HBM traffic (shader clock, MFMA busy "
-                         "fraction) from rocprofv3 --pmc runs")
+                    help="FETCH_DIR WRITE_DIR [CLOCK_DIR [SQ_DIR [RDREQ_DIR]]]: HBM traffic (shader clock, "
+                         "MFMA busy fraction, read bytes by request size) from rocprofv3 --pmc runs")
     args = ap.parse_args(argv)
 
     if args.summarize_pmc:
-        if len(args.summarize_pmc) not in (2, 3, 4):
-            ap.error("--summarize-pmc takes FETCH_DIR WRITE_DIR [CLOCK_DIR [SQ_DIR]]")
+        if len(args.summarize_pmc) not in (2, 3, 4, 5):
+            ap.error("--summarize-pmc takes FETCH_DIR WRITE_DIR [CLOCK_DIR [SQ_DIR [RDREQ_DIR]]]")
         return summarize_pmc(*args.summarize_pmc)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
@@ -404,7 +404,19 @@ def _clock_ghz(rows, name_part: str):
     return cyc / dur / 8.0 if dur > 0 else None
 
 
-def summarize_pmc(fetch_dir: str, write_dir: str, clock_dir: str | None = None, sq_dir: str | None = None) -> int:
+def _read_bytes_by_size(rows, name_part: str):
+    """Bytes read from EA per dispatch from the request-size counters (128/64/32-byte requests)."""
+    n, _ = _per_dispatch(rows, "TCC_EA0_RDREQ_sum", name_part)
+    r128, _ = _per_dispatch(rows, "TCC_EA0_RDREQ_128B_sum", name_part)
+    r64, _ = _per_dispatch(rows, "TCC_EA0_RDREQ_64B_sum", name_part)
+    r32, _ = _per_dispatch(rows, "TCC_EA0_RDREQ_32B_sum", name_part)
+    if None in (n, r128, r64, r32):
+        return None, None
+    return 128.0 * r128 + 64.0 * r64 + 32.0 * r32, n - r128 - r64 - r32
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, clock_dir: str | None = None, sq_dir: str | None = None,
+                  rdreq_dir: str | None = None) -> int:
     """HBM bytes per partial-kernel launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
     each scaled by what the same counter reads for the 1 GiB copy kernel; with a third run of
     GRBM_GUI_ACTIVE, also the shader clock the partial kernel ran at; with a fourth run of
@@ -412,8 +424,10 @@ def summarize_pmc(fetch_dir: str, write_dir: str, clock_dir: str | None = None, 
     fr, wr = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
     f_k, nf = _per_dispatch(fr, "FETCH_SIZE", "partial_bf16_d128_kernel")
     w_k, nw = _per_dispatch(wr, "WRITE_SIZE", "partial_bf16_d128_kernel")
-    f_c, _ = _per_dispatch(fr, "FETCH_SIZE", "elementwise")
-    w_c, _ = _per_dispatch(wr, "WRITE_SIZE", "elementwise")
+    # the copy kernel is torch's x * 1.0 over 1 GiB (MulFunctor); the fill that creates its
+    # source reads nothing and must not enter the calibration
+    f_c, _ = _per_dispatch(fr, "FETCH_SIZE", "MulFunctor")
+    w_c, _ = _per_dispatch(wr, "WRITE_SIZE", "MulFunctor")
     if None in (f_k, w_k, f_c, w_c):
         raise SystemExit("missing counters for the partial kernel or the copy kernel")
     f_scale = COPY_BYTES / (f_c * 1024.0)
@@ -424,8 +438,8 @@ def summarize_pmc(fetch_dir: str, write_dir: str, clock_dir: str | None = None, 
     with open(TRAFFIC_FILE, "w") as f:
         f.write("# HBM traffic of partial_bf16_d128_kernel per launch on the 128K-token workload, Pass-KV\n")
         f.write("# from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs of:\n")
-        f.write("#   python bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-decode --no-small --no-other-order --calibrate-copy\n")
-        f.write("# (every partial launch of that run is one Pass-KV ring step)\n")
+        f.write("#   python bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-small --no-other-order --calibrate-copy\n")
+        f.write("# (every partial launch of that run is one Pass-KV ring step; the decode leg runs after it)\n")
         f.write("# each counter scaled by its reading for a plain 1 GiB fp32 copy kernel\n")
         f.write(f"kernel_source_sha256_16: {kernel_hash()}\n")
         f.write(f"dispatches: {nf} (FETCH) {nw} (WRITE)\n")
@@ -436,9 +450,24 @@ def summarize_pmc(fetch_dir: str, write_dir: str, clock_dir: str | None = None, 
         f.write(f"fetch_bytes_per_launch: {fetch_b:.0f}\n")
         f.write(f"write_bytes_per_launch: {write_b:.0f}\n")
         f.write(f"hbm_bytes_per_launch: {fetch_b + write_b:.0f}\n")
+        d_f, nd = _per_dispatch(fr, "FETCH_SIZE", "decode_stream_kernel")
+        d_w, _ = _per_dispatch(wr, "WRITE_SIZE", "decode_stream_kernel")
+        if d_f is not None and d_w is not None:
+            f.write(f"# split-KV decode kernel of the same runs ({nd} dispatches), same calibration\n")
+            f.write(f"decode_fetch_bytes_per_launch: {d_f * 1024.0 * f_scale:.0f}\n")
+            f.write(f"decode_write_bytes_per_launch: {d_w * 1024.0 * w_scale:.0f}\n")
+        if rdreq_dir:
+            rr = _pmc_rows(rdreq_dir)
+            f.write("# cross-check from a run with TCC_EA0_RDREQ_{,128B_,64B_,32B_}sum: bytes read = 128/64/32 x\n"
+                    "# the requests of each size (no calibration; 'other' = requests of none of those sizes)\n")
+            for label, part in (("partial", "partial_bf16_d128_kernel"), ("decode", "decode_stream_kernel"),
+                                ("copy", "MulFunctor")):
+                rb, other = _read_bytes_by_size(rr, part)
+                if rb is not None:
+                    f.write(f"{label}_read_bytes_by_request_size: {rb:.0f} (other requests: {other:.0f})\n")
         if clock_dir:
             cr = _pmc_rows(clock_dir)
-            ck, cc = _clock_ghz(cr, "partial_bf16_d128_kernel"), _clock_ghz(cr, "elementwise")
+            ck, cc = _clock_ghz(cr, "partial_bf16_d128_kernel"), _clock_ghz(cr, "MulFunctor")
             f.write("# shader clock from a third run with --pmc GRBM_GUI_ACTIVE: busy clocks / 8 XCDs / dispatch time\n")
             f.write(f"sclk_ghz_partial_kernel: {ck:.3f}\n")
             f.write(f"sclk_ghz_copy_kernel: {cc:.3f}\n")
