@@ -287,6 +287,29 @@ def main(argv=None) -> int:
         log(f"[bench] {label} fused: {msf:.3f} ms")
         return msf
 
+    # the same Pass-KV ring with each partial merged into the running (O, LSE) by the kernel that
+    # computes it: 16 launches per step, no workspace and no merge pass
+    if not args.no_other_order:
+        for _ in range(2):
+            for s_ in range(P):
+                cp.ring_step_accumulate(gq, gk, gv, P, s_, out, lse, args.order, True)
+        torch.cuda.synchronize()
+        reps_a = max(3, args.steps // 2)
+        ev_a = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps_a)]
+        for i in range(reps_a):
+            ev_a[i][0].record(stream)
+            for s_ in range(P):
+                cp.ring_step_accumulate(gq, gk, gv, P, s_, out, lse, args.order, True)
+            ev_a[i][1].record(stream)
+        torch.cuda.synchronize()
+        ms_a = sorted(e[0].elapsed_time(e[1]) for e in ev_a)[reps_a // 2]
+        tf_a = total_flops / (ms_a * 1e-3) / 1e12
+        log(f"[bench] {w.name} accumulating ring steps: {ms_a:.3f} ms, {tf_a:.1f} TFLOP/s")
+        result["accumulate"] = {"ms_per_step": round(ms_a, 3), "TFLOP/s": round(tf_a, 2),
+                                "pct_bf16_peak": round(100 * tf_a / PEAK_BF16_TFLOPS, 2),
+                                "launch": "ring_step_accumulate x 16: each partial merged into the running "
+                                          "result by the kernel that computes it, no merge pass"}
+
     if not args.no_other_order:
         msf = fused_reps(gq, gk, gv, P, out, lse, max(3, args.steps // 2), w.name)
         result["fused"] = {"ms_per_step": round(msf, 3), "TFLOP/s": round(total_flops / (msf * 1e-3) / 1e12, 2),

@@ -63,6 +63,7 @@ def _load() -> ctypes.CDLL:
         "cpattn_ring_step": ([P, P, P, i32, i32, i32, i32, vp, sz, vp], i32),
         "cpattn_ring_merge": ([i32, i32, i32, vp, sz, P, P, vp], i32),
         "cpattn_ring_prefill_fused": ([P, P, P, i32, i32, P, P, vp], i32),
+        "cpattn_ring_step_accumulate": ([P, P, P, i32, i32, i32, i32, P, P, vp], i32),
         "cpattn_splitkv_decode_workspace_size": ([P, P, i32], sz),
         "cpattn_splitkv_decode": ([P, P, P, i32, P, P, vp, sz, vp], i32),
         "cpattn_last_error": ([], ctypes.c_char_p),
@@ -198,6 +199,16 @@ def ring_step(q, k, v, n_chunks: int, step: int, workspace, order="pass_kv", cau
     _check(lib.cpattn_ring_step(_ref(dq), _ref(dk), _ref(dv), int(n_chunks), _ORDERS[order], int(bool(causal)),
                                 int(step), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                 _stream(q, stream)))
+
+
+def ring_step_accumulate(q, k, v, n_chunks: int, step: int, out, lse, order="pass_kv", causal: bool = True,
+                         stream=None):
+    """Ring step ``step`` with each pair's partial merged into the running ``out``/``lse`` (fp32):
+    step 0 writes, later steps merge; after steps 0..n_chunks-1 they hold the full result."""
+    dq, dk, dv, do, dl = describe(q), describe(k), describe(v), describe(out), describe(lse, True)
+    _check(lib.cpattn_ring_step_accumulate(_ref(dq), _ref(dk), _ref(dv), int(n_chunks), _ORDERS[order],
+                                           int(bool(causal)), int(step), _ref(do), _ref(dl), _stream(q, stream)))
+    return out, lse
 
 
 def ring_merge(n_chunks: int, workspace, out, lse=None, order="pass_kv", causal: bool = True, stream=None):

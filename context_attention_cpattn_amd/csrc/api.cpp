@@ -416,6 +416,37 @@ cpattn_status cpattn_ring_step(const cpattn_tensor* q, const cpattn_tensor* k, c
                            "ring step launch");
 }
 
+cpattn_status cpattn_ring_step_accumulate(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                                          int n_chunks, cpattn_order order, int causal, int step,
+                                          cpattn_tensor* out, cpattn_tensor* lse, void* stream) {
+  cpattn_status s;
+  if ((s = check_ring(q, k, v, n_chunks, order, causal)) != CPATTN_OK) return s;
+  if (step < 0 || step >= n_chunks) return fail(CPATTN_ERR_INVALID_ARG, "step %d outside [0, %d)", step, n_chunks);
+  if ((s = check_out(out, lse, *q, false, true)) != CPATTN_OK) return s;
+  if (q->S == 0 || q->B == 0) return ok();
+  const bool cz = causal != 0;
+  const int64_t C = q->S / n_chunks;
+  cpattn::PartialLaunch a = base_partial(*q, *k, *v);
+  a.o = static_cast<float*>(out->data);
+  a.o_sb = out->stride_b; a.o_ss = out->stride_s; a.o_sh = out->stride_h;
+  a.o_slot = C * out->stride_s;  // owner i's rows start at row iC
+  a.lse = static_cast<float*>(lse->data);
+  a.l_sb = lse->stride_b; a.l_ss = lse->stride_s; a.l_sh = lse->stride_h;
+  a.l_slot = C * lse->stride_s;
+  a.chunk_len = C;
+  a.Sq = (int32_t)C;
+  a.Sk = (int32_t)C;
+  a.causal = cz ? 1 : 0;
+  // step 0 is every owner's first arrival (its own chunk): it writes; later steps merge
+  a.accumulate = step > 0 ? 1 : 0;
+  a.n_items = 0;
+  for (const Pair& p : ring_step(n_chunks, step, order, cz)) a.items[a.n_items++] = cpattn::Item{p.q, p.kv, p.q, 0};
+  if (a.n_items == 0) return ok();
+  const hipError_t e = launch_partial(a, q->dtype, (int)q->D, (int)C, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "accumulating ring step launch");
+  return ok();
+}
+
 cpattn_status cpattn_ring_merge(int n_chunks, cpattn_order order, int causal, const void* workspace,
                                 size_t workspace_bytes, cpattn_tensor* out, cpattn_tensor* lse, void* stream) {
   cpattn_status s;

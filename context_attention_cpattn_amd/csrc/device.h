@@ -93,6 +93,28 @@ __device__ __forceinline__ float pair32_sum(float x) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
+// How a finished row is written.  The kernel holds an unnormalised
+// accumulator relative to the base-2 reference m2 and the row sum l.  A plain
+// store writes O = acc / l and LSE = (m2 + log2 l) ln 2 (-inf and O = 0 for a
+// row with no visible key).  An accumulating store merges that partial with
+// the normalised O and natural-log LSE already at the destination, exactly
+// (up to rounding) as the LSE merge does: with M the larger of the two LSEs,
+// O = (O_old w_old + O_new w_new) / (w_old + w_new), w = exp(LSE - M), and
+// LSE = M + ln(w_old + w_new).  Every output value is acc * s_new + old * s_old.
+struct RowOut {
+  float s_new, s_old, lse;
+};
+__device__ __forceinline__ RowOut row_out(float m2, float l, bool accumulate, float lse_old) {
+  const float lse2 = (l > 0.f) ? m2 + fast_log2(l) : kNegInf;
+  if (!accumulate) return RowOut{(l > 0.f) ? 1.f / l : 0.f, 0.f, (l > 0.f) ? lse2 * kLn2 : kNegInf};
+  const float old2 = lse_old * kLog2e;
+  const float mx = fmaxf(lse2, old2);
+  if (mx == kNegInf) return RowOut{0.f, 0.f, kNegInf};
+  const float wn = fast_exp2(lse2 - mx), wo = fast_exp2(old2 - mx);
+  const float t = 1.f / (wn + wo);
+  return RowOut{(l > 0.f) ? wn * t / l : 0.f, wo * t, (mx + fast_log2(wn + wo)) * kLn2};
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup w runs on
 // XCD w % 8).  Give each XCD a contiguous range of logical tiles so tiles that
 // share K/V (adjacent heads of one query tile) share that XCD's L2.

@@ -9,6 +9,7 @@ namespace cpattn {
 
 constexpr int kMaxItems = 160;  // partial-attention work items per launch (kernel argument ~2.8 KB)
 constexpr int kMaxMerge = 64;   // partials per merge launch (CPATTN_MAX_MERGE)
+static_assert(kMaxMerge <= kMaxItems, "the pairs of one ring step (at most kMaxMerge) fit one launch");
 
 // One (Q block, K/V block) pair of a launch.  Pointers are derived from the
 // launch's base pointers: Q rows start at q_chunk * chunk_len, K/V rows at
@@ -38,6 +39,7 @@ struct PartialLaunch {
   int32_t causal;
   int32_t n_items;
   int32_t xcd_order;  // 1: each XCD takes a contiguous share of the grid; 0: launch order
+  int32_t accumulate; // 1: merge into the (O, LSE) already at the destination (lse not null)
   Item items[kMaxItems];
 };
 

@@ -279,18 +279,25 @@ __global__ __launch_bounds__(256) void partial_bf16_kernel(const PartialLaunch a
   // ---- epilogue: combine the two half-rows' sums, normalise, store
   const float l_tot = l_run + xor32(l_run);
   if (row < a.Sq) {
-    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    const bool acc = a.accumulate != 0;
+    const RowOut ro = row_out(m_run, l_tot, acc, acc ? lp[(int64_t)row * a.l_ss] : 0.f);
     float* orow = op + (int64_t)row * a.o_ss;
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        const f32x4 v4 = {oacc[db][4 * i4 + 0] * inv, oacc[db][4 * i4 + 1] * inv, oacc[db][4 * i4 + 2] * inv,
-                          oacc[db][4 * i4 + 3] * inv};
-        *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * i4 + 4 * g) = v4;
+        float* dst = orow + db * 32 + 8 * i4 + 4 * g;
+        f32x4 v4 = {oacc[db][4 * i4 + 0] * ro.s_new, oacc[db][4 * i4 + 1] * ro.s_new, oacc[db][4 * i4 + 2] * ro.s_new,
+                    oacc[db][4 * i4 + 3] * ro.s_new};
+        if (acc) {
+          const f32x4 old = *reinterpret_cast<const f32x4*>(dst);
+          v4 = (f32x4){fmaf(old[0], ro.s_old, v4[0]), fmaf(old[1], ro.s_old, v4[1]), fmaf(old[2], ro.s_old, v4[2]),
+                       fmaf(old[3], ro.s_old, v4[3])};
+        }
+        *reinterpret_cast<f32x4*>(dst) = v4;
       }
     }
-    if (g == 0 && lp != nullptr) lp[(int64_t)row * a.l_ss] = (l_tot > 0.f) ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
+    if (g == 0 && lp != nullptr) lp[(int64_t)row * a.l_ss] = ro.lse;
   }
 }
 
@@ -682,17 +689,24 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
 
   const float l_tot = pair32_sum(l);
   if (row < a.Sq) {
-    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    const bool acc = a.accumulate != 0;
+    const RowOut ro = row_out(m, l_tot, acc, acc ? lp[(int64_t)row * a.l_ss] : 0.f);
     float* orow = op + (int64_t)row * a.o_ss;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        const f32x4 v4 = {o[db][4 * i4 + 0] * inv, o[db][4 * i4 + 1] * inv, o[db][4 * i4 + 2] * inv,
-                          o[db][4 * i4 + 3] * inv};
-        *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * i4 + 4 * g) = v4;
+        float* dst = orow + db * 32 + 8 * i4 + 4 * g;
+        f32x4 v4 = {o[db][4 * i4 + 0] * ro.s_new, o[db][4 * i4 + 1] * ro.s_new, o[db][4 * i4 + 2] * ro.s_new,
+                    o[db][4 * i4 + 3] * ro.s_new};
+        if (acc) {
+          const f32x4 old = *reinterpret_cast<const f32x4*>(dst);
+          v4 = (f32x4){fmaf(old[0], ro.s_old, v4[0]), fmaf(old[1], ro.s_old, v4[1]), fmaf(old[2], ro.s_old, v4[2]),
+                       fmaf(old[3], ro.s_old, v4[3])};
+        }
+        *reinterpret_cast<f32x4*>(dst) = v4;
       }
-    if (g == 0 && lp != nullptr) lp[(int64_t)row * a.l_ss] = (l_tot > 0.f) ? (m + fast_log2(l_tot)) * kLn2 : kNegInf;
+    if (g == 0 && lp != nullptr) lp[(int64_t)row * a.l_ss] = ro.lse;
   }
 }
 

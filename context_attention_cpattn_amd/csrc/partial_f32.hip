@@ -111,12 +111,20 @@ __global__ __launch_bounds__(256) void partial_f32_kernel(const PartialLaunch a,
   }
 
   if (row_ok) {
-    const float inv = (l > 0.f) ? 1.f / l : 0.f;
+    const bool acc = a.accumulate != 0;
+    const RowOut ro = row_out(m, l, acc, acc ? lp[(int64_t)row * a.l_ss] : 0.f);
     float* orow = op + (int64_t)row * a.o_ss + 32 * part;
 #pragma unroll
-    for (int x = 0; x < 32; x += 4)
-      *reinterpret_cast<f32x4*>(orow + x) = (f32x4){o[x] * inv, o[x + 1] * inv, o[x + 2] * inv, o[x + 3] * inv};
-    if (part == 0 && lp != nullptr) lp[(int64_t)row * a.l_ss] = (l > 0.f) ? (m + fast_log2(l)) * kLn2 : kNegInf;
+    for (int x = 0; x < 32; x += 4) {
+      f32x4 v4 = {o[x] * ro.s_new, o[x + 1] * ro.s_new, o[x + 2] * ro.s_new, o[x + 3] * ro.s_new};
+      if (acc) {
+        const f32x4 old = *reinterpret_cast<const f32x4*>(orow + x);
+        v4 = (f32x4){fmaf(old[0], ro.s_old, v4[0]), fmaf(old[1], ro.s_old, v4[1]), fmaf(old[2], ro.s_old, v4[2]),
+                     fmaf(old[3], ro.s_old, v4[3])};
+      }
+      *reinterpret_cast<f32x4*>(orow + x) = v4;
+    }
+    if (part == 0 && lp != nullptr) lp[(int64_t)row * a.l_ss] = ro.lse;
   }
 }
 

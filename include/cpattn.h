@@ -168,6 +168,29 @@ cpattn_status cpattn_ring_step(const cpattn_tensor* q, const cpattn_tensor* k, c
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * cpattn_ring_step_accumulate - one ring step whose partials are merged into
+ * the running result as they arrive, with no workspace and no separate merge:
+ * the kernel that computes a pair's partial (O, LSE) combines it with the
+ * owner's rows already in out/lse by the exact LSE merge (techreport.ngo
+ * rewrite, "Context Parallelism for Million-Token Contexts": the per-pair
+ * partial results are accumulated into the full attention result).  Step 0
+ * gives every owner its first pair (its own chunk) and writes those rows;
+ * each later step merges the pair it assigns into them.  Running steps
+ * 0 .. n_chunks-1 in order on one stream leaves the full attention in out and
+ * lse, merged in arrival order (the order cpattn_ring_merge uses); rows of an
+ * owner with no pair at a step are not touched.
+ *   q, k, v, n_chunks, order, causal, step  as in cpattn_ring_step
+ *   out [B, S, Hq, D]  F32 (read and written from step 1 on)
+ *   lse [B, S, Hq]     F32, required (the running LSE)
+ * Steps after 0 read out/lse as left by the earlier steps of the same ring:
+ * calls for one ring must not overlap, and nothing else may write out/lse in
+ * between.
+ */
+cpattn_status cpattn_ring_step_accumulate(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                                          int n_chunks, cpattn_order order, int causal, int step,
+                                          cpattn_tensor* out, cpattn_tensor* lse, void* stream);
+
+/*
  * cpattn_ring_merge - merge every Q chunk's partials from a workspace filled
  * by cpattn_ring_step (all steps), in the order they reached the chunk's
  * owner, into out [B, S, Hq, D] (F32 or BF16) and lse [B, S, Hq] (F32, or

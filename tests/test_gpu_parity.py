@@ -176,6 +176,33 @@ def test_ring_merge_follows_arrival_order(cp, P, order, causal):
         assert torch.equal(lm, l[:, i * C:(i + 1) * C]), f"owner {i}: LSE differs"
 
 
+@pytest.mark.parametrize("P,order,causal,D,dtype", [(1, "pass_kv", True, 128, "bf16"), (4, "pass_kv", True, 128, "bf16"),
+                                                  (4, "pass_q", True, 128, "bf16"), (5, "pass_kv", False, 128, "bf16"),
+                                                  (3, "pass_q", False, 64, "bf16"), (6, "pass_kv", True, 64, "bf16"),
+                                                  (4, "pass_q", True, 64, "f32"), (3, "pass_kv", False, 128, "f32")])
+def test_ring_step_accumulate(cp, P, order, causal, D, dtype):
+    """Ring steps that merge each arriving partial into the running (O, LSE): after all steps the
+    result is the full attention, and it matches the partials-then-merge driver to fp32 rounding."""
+    S = 120 * P
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q = draw(91 + P, (2, S, 4, D), tdt, 0)
+    k = draw(91 + P, (2, S, 2, D), tdt, 1)
+    v = draw(91 + P, (2, S, 2, D), tdt, 2)
+    o_ref, l_ref = oracle.full_attention(q, k, v, causal)
+    gq, gk, gv = q.to(DEV), k.to(DEV), v.to(DEV)
+    out = torch.full((2, S, 4, D), float("nan"), device=DEV)  # step 0 must write every row
+    lse = torch.full((2, S, 4), float("nan"), device=DEV)
+    banner("ring accumulate", P, order, causal, D, dtype)
+    for step in range(P):
+        cp.ring_step_accumulate(gq, gk, gv, P, step, out, lse, order, causal)
+    torch.cuda.synchronize()
+    compare(out, lse, o_ref, l_ref, BF16_TOL if dtype == "bf16" else F32_TOL,
+            f"ring accumulate P={P} {order} causal={causal} D={D} {dtype}")
+    o2, l2 = cp.ring_prefill(gq, gk, gv, P, order, causal)
+    torch.cuda.synchronize()
+    assert (o2 - out).abs().max().item() <= 1e-5 and (l2 - lse).abs().max().item() <= 1e-5
+
+
 @pytest.mark.parametrize("P,causal,Hkv,D", [(1, True, 1, 128), (4, True, 2, 128), (5, False, 1, 128), (3, True, 1, 64),
                                            (6, True, 4, 64), (64, True, 1, 128), (64, False, 2, 64)])
 def test_ring_prefill_fused(cp, P, causal, Hkv, D):
@@ -279,6 +306,20 @@ def test_workload_128k_both_orders(cp):
     print(f"[parity] {w.name}: pass_kv vs pass_q max|dO|={d_o:.3e} max|dLSE|={d_l:.3e}", flush=True)
     assert d_o <= 1e-5 and d_l <= 1e-5
     del oq, lq
+    # the accumulating ring steps (each partial merged into the running result by the kernel that
+    # computes it): same sampled rows against the oracle, every row against the per-pair path
+    banner(w.name, "ring_step_accumulate", w.n_chunks)
+    oa = torch.empty_like(okv)
+    la = torch.empty_like(lkv)
+    for step in range(w.n_chunks):
+        cp.ring_step_accumulate(gq, gk, gv, w.n_chunks, step, oa, la, "pass_kv", True)
+    torch.cuda.synchronize()
+    _sampled_check(cp, w, oa, la, q, k, v, f"{w.name} accumulate")
+    d_o = (okv - oa).abs().max().item()
+    d_l = (lkv - la).abs().max().item()
+    print(f"[parity] {w.name}: accumulate vs pass_kv max|dO|={d_o:.3e} max|dLSE|={d_l:.3e}", flush=True)
+    assert d_o <= 1e-5 and d_l <= 1e-5
+    del oa, la
     # the fused ring prefill (online merge, one launch): the same sampled rows against the oracle,
     # and every row against the per-pair path.  The two round P to bf16 against different running
     # maxima, so they differ by bf16 rounding of P, not by fp32 reordering alone: the bar between
