@@ -185,6 +185,36 @@ def test_ring_validation():
 
 
 @no_gpu
+def test_ring_online_merge_validation():
+    """The accumulating ring step and the fused prefill check their arguments before any launch."""
+    r = ctypes.byref
+    q, k, v = bshd(1, 512, 4, 64), bshd(1, 512, 1, 64), bshd(1, 512, 1, 64)
+    out, lse = bshd(1, 512, 4, 64, cp.DT_F32), lse_of(1, 512, 4)
+
+    def acc(n=4, step=1, order=0, causal=1, lse_=lse, out_=out):
+        return lib.cpattn_ring_step_accumulate(r(q), r(k), r(v), n, order, causal, step, r(out_),
+                                               r(lse_) if lse_ else None, None)
+
+    assert acc(lse_=None) == cp.ERR_INVALID_ARG and "lse" in err()  # the running LSE is required
+    assert acc(step=4) == cp.ERR_INVALID_ARG and "step" in err()
+    assert acc(step=-1) == cp.ERR_INVALID_ARG
+    assert acc(n=3) == cp.ERR_INVALID_ARG
+    assert acc(n=128) == cp.ERR_UNSUPPORTED
+    assert acc(order=5) == cp.ERR_INVALID_ARG
+    assert acc(out_=bshd(1, 512, 4, 64)) == cp.ERR_INVALID_ARG  # a bf16 running output is refused
+    assert acc(out_=bshd(1, 256, 4, 64, cp.DT_F32)) == cp.ERR_INVALID_ARG
+
+    def fused(n=4, causal=1, lse_=lse, out_=out):
+        return lib.cpattn_ring_prefill_fused(r(q), r(k), r(v), n, causal, r(out_), r(lse_) if lse_ else None, None)
+
+    assert fused(n=3) == cp.ERR_INVALID_ARG
+    assert fused(n=0) == cp.ERR_INVALID_ARG
+    assert fused(causal=2) == cp.ERR_INVALID_ARG
+    assert fused(out_=bshd(1, 512, 4, 64)) == cp.ERR_INVALID_ARG
+    assert fused(lse_=lse_of(1, 512, 3)) == cp.ERR_INVALID_ARG
+
+
+@no_gpu
 def test_decode_validation():
     r = ctypes.byref
     q, k, v = bshd(4, 1, 16, 128), bshd(4, 4096, 1, 128), bshd(4, 4096, 1, 128)
