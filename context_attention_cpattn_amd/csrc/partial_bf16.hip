@@ -316,8 +316,10 @@ __global__ __launch_bounds__(256) void partial_bf16_kernel(const PartialLaunch a
 // so when lane s addresses row key0 + s/4 at columns D0 + 4(s%4), lane i
 // receives V[key0 .. key0+3][D0 + i] -- four keys of one column.
 //
-// LDS stage = K tile (64 keys x 256 B, 16-byte chunks XOR-swizzled by
-// key & 15) + V tile (64 keys x 256 B, chunks XOR-swizzled by 4 (key & 3)).
+// LDS: the K tiles of the three stages (64 keys x 256 B each, 16-byte chunks
+// XOR-swizzled by key & 15), then their V tiles (chunks XOR-swizzled by
+// 4 (key & 3)); with K and V apart, every operand read reaches its data
+// through the 16-bit offset of ds_read from one per-lane base.
 //
 // Each wave's work is software-pipelined so that its matrix and vector work
 // overlap.  Iteration t runs two phases:
@@ -371,14 +373,16 @@ __device__ __forceinline__ void pin(T& x) {
 __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLaunch a, const int n_qtiles) {
   constexpr int D = 128, BN = 64, NDS = 8, BM = 256;
   constexpr int TBYTES = BN * D * 2;  // one K or V tile
-  constexpr int STAGE = 2 * TBYTES;   // K then V
   constexpr int NST = 3;              // LDS stages: tile t+2 is fetched while t and t+1 are read
+  // LDS: the K tiles of all stages, then the V tiles, so every operand read's
+  // offset from its per-lane base fits the 16-bit immediate of ds_read
+  constexpr int VBASE = NST * TBYTES;
   constexpr int KLA = 4;              // K operand reads issued this many MFMAs ahead
   constexpr int VLA = 4;              // V operand reads issued this many MFMAs ahead
   constexpr int FW = 4;               // fetching waves
   constexpr int FL = 1024 / (FW * 64);  // 16-byte pieces of K (and of V) per fetching lane
   constexpr float SCALE_LOG2 = 0.12751743082459868f;  // log2(e) / sqrt(128)
-  __shared__ __attribute__((aligned(16))) uint8_t smem[NST * STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * NST * TBYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -443,7 +447,7 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
     {
       const int s16 = lane & 15, ks = s16 >> 2, c16 = l32 >> 4, c8 = (s16 & 3) >> 1, bo = (s16 & 1) * 8;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) voff[db] = TBYTES + (4 * g + ks) * 256 + ((4 * (db ^ ks) + 2 * c16 + c8) << 4) + bo;
+      for (int db = 0; db < 4; ++db) voff[db] = VBASE + (4 * g + ks) * 256 + ((4 * (db ^ ks) + 2 * c16 + c8) << 4) + bo;
     }
     // Fetch: piece i of fetching wave fw, lane l is tile slot i*FW*64 + fw*64 + l,
     // which holds key slot>>4 at physical chunk slot&15 (logical chunk for K:
@@ -464,13 +468,13 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
     const uint32_t lbase = lds_addr(smem) + (wave % FW) * 64 * 16;
     int n_fetched = 0;
     auto fetch = [&](int stage) {
-      const uint32_t dst = lbase + stage * STAGE;
+      const uint32_t dst = lbase + stage * TBYTES;
       if (fetcher) {
         if ((n_fetched + 1) * BN <= Sk) {
 #pragma unroll
           for (int i = 0; i < FL; ++i) {
             gload_lds16(kf[i], dst + i * FW * 64 * 16);
-            gload_lds16(vf[i], dst + i * FW * 64 * 16 + TBYTES);
+            gload_lds16(vf[i], dst + i * FW * 64 * 16 + VBASE);
           }
         } else {
           // rows past the block end re-read the last row: their scores are
@@ -479,7 +483,7 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
           for (int i = 0; i < FL; ++i) {
             const int over = max(0, n_fetched * BN + fkey[i] - (Sk - 1));
             gload_lds16(kf[i] - over * a.k_ss, dst + i * FW * 64 * 16);
-            gload_lds16(vf[i] - over * a.v_ss, dst + i * FW * 64 * 16 + TBYTES);
+            gload_lds16(vf[i] - over * a.v_ss, dst + i * FW * 64 * 16 + VBASE);
           }
         }
 #pragma unroll
@@ -575,8 +579,8 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
       constexpr int ST = decltype(st_tag)::value;
       constexpr int SN = (ST + 1) % NST;
       constexpr int SL = (ST + NST - 1) % NST;
-      const uint8_t* cur = smem + ST * STAGE;
-      const uint8_t* nxt = smem + SN * STAGE;
+      const uint8_t* cur = smem + ST * TBYTES;  // K of tile t at cur, V at cur + VBASE (voff)
+      const uint8_t* nxt = smem + SN * TBYTES;
       STAMP(wave, t, 0, L);
       // tile t+2 goes into the stage tile t-1 used
       const bool do_fetch = t + NST - 1 < n_tiles;
