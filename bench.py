@@ -78,21 +78,22 @@ def read_pmc_summary():
     """(HBM bytes per launch, shader clock GHz, MFMA busy fraction) of the partial kernel from the
     committed pmc summary, each None if absent or if the kernel source changed since it was taken."""
     if not os.path.exists(TRAFFIC_FILE):
-        return None, None, None
+        return None, None, None, None
     kv = {}
     for ln in open(TRAFFIC_FILE):
         if ":" in ln and not ln.startswith("#"):
             a, b = ln.split(":", 1)
             kv[a.strip()] = b.strip()
     if kv.get("kernel_source_sha256_16") != kernel_hash():
-        return None, None, None
+        return None, None, None, None
 
     def num(key):
         try:
             return float(kv[key])
         except (KeyError, ValueError):
             return None
-    return num("hbm_bytes_per_launch"), num("sclk_ghz_partial_kernel"), num("mfma_busy_fraction")
+    return (num("hbm_bytes_per_launch"), num("sclk_ghz_partial_kernel"), num("mfma_busy_fraction"),
+            num("frac_of_peak_at_measured_sclk"))
 
 
 def cpu_baseline(w, q, k, v, seconds: float):
@@ -152,8 +153,8 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.summarize_pmc:
-        if len(args.summarize_pmc) not in (2, 3, 4, 5):
-            ap.error("--summarize-pmc takes FETCH_DIR WRITE_DIR [CLOCK_DIR [SQ_DIR [RDREQ_DIR]]]")
+        if len(args.summarize_pmc) not in (2, 3, 4, 5, 6):
+            ap.error("--summarize-pmc takes FETCH_DIR WRITE_DIR [CLOCK_DIR [SQ_DIR [RDREQ_DIR [TRACE_DIR]]]]")
         return summarize_pmc(*args.summarize_pmc)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
@@ -215,16 +216,16 @@ def main(argv=None) -> int:
     launches = args.steps * P
     avg_launch_ms = kern_ms_total / launches
     achieved = total_flops * args.steps / (kern_ms_total * 1e-3) / 1e12
-    traffic, sclk, mfma_busy = read_pmc_summary()
+    traffic, sclk, mfma_busy, frac_sclk = read_pmc_summary()
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 # the chip does not hold 2.4 GHz under this kernel: the same fraction against the dense
                 # peak at the shader clock measured for it (rocprofv3 GRBM_GUI_ACTIVE, profiles/)
                 "sclk_ghz_measured": sclk,
-                "sclk_source": ("rocprofv3 GRBM_GUI_ACTIVE run of this kernel source on another box "
-                                "(profiles/partial_bf16_prefill_s128k_p16_traffic.txt); boxes differ by ~5%"
-                                if sclk else None),
-                "frac_at_measured_sclk": (round(achieved / (PEAK_BF16_TFLOPS * sclk / 2.4), 4) if sclk else None),
+                "sclk_source": ("rocprofv3 GRBM_GUI_ACTIVE run of this kernel source, and the kernel trace "
+                                "taken beside it on the same box (profiles/partial_bf16_prefill_s128k_p16_traffic.txt); "
+                                "boxes differ by up to ~7%" if sclk else None),
+                "frac_at_measured_sclk": frac_sclk,
                 "mfma_busy_fraction_profiled": mfma_busy,
                 "kernel": "partial_bf16_d128_kernel", "launches_per_step": P,
                 "avg_launch_ms": round(avg_launch_ms, 4),
@@ -405,6 +406,11 @@ def main(argv=None) -> int:
     return 0
 
 
+def _prefill_workload():
+    import seeded_inputs as si
+    return si.WORKLOADS[PREFILL]
+
+
 def _pmc_rows(d: str):
     rows = []
     for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
@@ -444,7 +450,7 @@ def _read_bytes_by_size(rows, name_part: str):
 
 
 def summarize_pmc(fetch_dir: str, write_dir: str, clock_dir: str | None = None, sq_dir: str | None = None,
-                  rdreq_dir: str | None = None) -> int:
+                  rdreq_dir: str | None = None, trace_dir: str | None = None) -> int:
     """HBM bytes per partial-kernel launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
     each scaled by what the same counter reads for the 1 GiB copy kernel; with a third run of
     GRBM_GUI_ACTIVE, also the shader clock the partial kernel ran at; with a fourth run of
@@ -499,6 +505,24 @@ def summarize_pmc(fetch_dir: str, write_dir: str, clock_dir: str | None = None, 
             f.write("# shader clock from a third run with --pmc GRBM_GUI_ACTIVE: busy clocks / 8 XCDs / dispatch time\n")
             f.write(f"sclk_ghz_partial_kernel: {ck:.3f}\n")
             f.write(f"sclk_ghz_copy_kernel: {cc:.3f}\n")
+            if trace_dir:
+                # the kernel trace of the same box: its average partial-kernel launch against the dense
+                # peak at the clock above (both from this box, unlike a live bench run elsewhere)
+                stats = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+                avg_ns = None
+                for path in stats:
+                    with open(path, newline="") as sf:
+                        for r in csv.DictReader(sf):
+                            if "partial_bf16_d128_kernel" in r.get("Name", ""):
+                                avg_ns = float(r["AverageNs"])
+                if avg_ns:
+                    w = _prefill_workload()
+                    tf = w.flops() / w.n_chunks / (avg_ns * 1e-9) / 1e12
+                    f.write("# the kernel trace of the same box: average partial-kernel launch, its rate, and that\n"
+                            "# rate against the dense bf16 peak scaled to the clock above\n")
+                    f.write(f"trace_avg_ms_partial_kernel: {avg_ns / 1e6:.4f}\n")
+                    f.write(f"trace_tflops_partial_kernel: {tf:.1f}\n")
+                    f.write(f"frac_of_peak_at_measured_sclk: {tf / (PEAK_BF16_TFLOPS * ck / 2.4):.4f}\n")
         if sq_dir:
             sr = _pmc_rows(sq_dir)
             k = "partial_bf16_d128_kernel"
