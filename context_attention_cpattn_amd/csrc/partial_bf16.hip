@@ -504,9 +504,12 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
       }
     };
 
-    f32x16 sn[2];       // scores of the newest tile
-    uint32_t pw[16];    // packed P of the tile being accumulated (word w: p[2w], p[2w+1];
-                        // words 0..7 from key block 0, 8..15 from key block 1)
+    // Two sets of tile state, used alternately by even and odd iterations so
+    // that no iteration copies registers into the next: scores of the newest
+    // tile, and packed P of the tile being accumulated (word w: p[2w], p[2w+1];
+    // words 0..7 from key block 0, 8..15 from key block 1).
+    f32x16 snA[2], snB[2];
+    uint32_t pwA[16], pwB[16];
     float lt = 0.f;     // this lane's partial sum of that tile
     bool need = false;  // O must be rescaled by alpha before the next PV
     float alpha = 1.f;
@@ -539,7 +542,7 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
       need = true;
     };
     // the slow path for tile t (its K and mask), recomputing all of pw and lt
-    auto redo_tile = [&](const uint8_t* kbase, int t) {
+    auto redo_tile = [&](const uint8_t* kbase, int t, uint32_t (&pw)[16]) {
       f32x16 sc[2];
       scores(kbase, sc);
       mask_tile(sc, t);
@@ -559,15 +562,15 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
       if (i < n_tiles) fetch(i);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     {
-      scores(smem, sn);
-      mask_tile(sn, 0);
-      move_to_max(sn);
+      scores(smem, snA);
+      mask_tile(snA, 0);
+      move_to_max(snA);
       need = false;  // O is still zero
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
-        const float p0 = prob(sn[0][2 * w]);
-        const float p1 = prob(sn[0][2 * w + 1]);
-        pw[w] = pack_bf16(p0, p1);
+        const float p0 = prob(snA[0][2 * w]);
+        const float p1 = prob(snA[0][2 * w + 1]);
+        pwA[w] = pack_bf16(p0, p1);
       }
     }
 
@@ -575,7 +578,8 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
     // last: every one of them is masked (that tile starts at or past the
     // block's last visible key), so its probabilities are 0; its K operands
     // come from a stale stage that no fetch is writing.
-    auto iteration = [&](int t, auto st_tag) {
+    auto iteration = [&](int t, auto st_tag, f32x16 (&sn)[2], f32x16 (&x)[2], uint32_t (&pw)[16],
+                         uint32_t (&pn)[16]) {
       constexpr int ST = decltype(st_tag)::value;
       constexpr int SN = (ST + 1) % NST;
       constexpr int SL = (ST + NST - 1) % NST;
@@ -595,8 +599,9 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
       };
       // ---- phase A: S(t+1) = K(t+1) Q^T; key block 1 of P(t) ----
       __builtin_amdgcn_s_setprio(1);
-      const f32x16 s1 = sn[1];
-      f32x16 x[2] = {(f32x16){}, (f32x16){}};
+      const f32x16& s1 = sn[1];
+      x[0] = (f32x16){};
+      x[1] = (f32x16){};
 #pragma unroll
       for (int j = 0; j < KLA; ++j) kop[j] = ld_lds16(nxt + koff[j >> 1] + (j & 1) * 8192);
       float pe = 0.f, pp = 0.f;
@@ -629,11 +634,9 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
       }
       lt += pp;
       pw[15] = pack_bf16(pe, pp);
-      sn[0] = x[0];
-      sn[1] = x[1];
-      mask_tile(sn, t + 1);
+      mask_tile(x, t + 1);
       // tile t is complete: keep it, or take the slow path
-      if (__any(!(lt <= kTwoTau) || m == kNegInf)) redo_tile(cur, t);
+      if (__any(!(lt <= kTwoTau) || m == kNegInf)) redo_tile(cur, t, pw);
       l += lt;
       lt = 0.f;
       __builtin_amdgcn_sched_barrier(0);
@@ -646,8 +649,7 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
         for (int db = 0; db < 4; ++db) o[db] *= alpha;
         need = false;
       }
-      uint32_t pn[8];
-      xa = fmaf(sn[0][0], SCALE_LOG2, -mref);
+      xa = fmaf(x[0][0], SCALE_LOG2, -mref);
       pin(xa);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -658,7 +660,7 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
         const u32x4 bp = {pw[4 * u], pw[4 * u + 1], pw[4 * u + 2], pw[4 * u + 3]};
         o[db] = mfma32(as_bf16x8(av), as_bf16x8(bp), o[db]);
         const float pv = fast_exp2(xa);
-        if (jj < 15) xa = fmaf(sn[0][jj + 1], SCALE_LOG2, -mref);
+        if (jj < 15) xa = fmaf(x[0][jj + 1], SCALE_LOG2, -mref);
         if (jj > 0) {
           lt += pp;
           if ((jj - 1) & 1) {
@@ -677,17 +679,20 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
       }
       lt += pp;
       pn[7] = pack_bf16(pe, pp);
-#pragma unroll
-      for (int w = 0; w < 8; ++w) pw[w] = pn[w];
       STAMP(wave, t, 2, L);
       // tile t+2 (fetched above) must have landed before any wave reads it
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
       STAMP(wave, t, 3, L);
     };
-    for (int t = 0; t < n_tiles; t += NST) {
-      iteration(t, std::integral_constant<int, 0>{});
-      if (t + 1 < n_tiles) iteration(t + 1, std::integral_constant<int, 1>{});
-      if (t + 2 < n_tiles) iteration(t + 2, std::integral_constant<int, 2>{});
+    // six iterations per trip: three LDS stages times two register sets
+    static_assert(NST == 3, "the loop below is unrolled over three stages");
+    for (int t = 0; t < n_tiles; t += 2 * NST) {
+      iteration(t, std::integral_constant<int, 0>{}, snA, snB, pwA, pwB);
+      if (t + 1 < n_tiles) iteration(t + 1, std::integral_constant<int, 1>{}, snB, snA, pwB, pwA);
+      if (t + 2 < n_tiles) iteration(t + 2, std::integral_constant<int, 2>{}, snA, snB, pwA, pwB);
+      if (t + 3 < n_tiles) iteration(t + 3, std::integral_constant<int, 0>{}, snB, snA, pwB, pwA);
+      if (t + 4 < n_tiles) iteration(t + 4, std::integral_constant<int, 1>{}, snA, snB, pwA, pwB);
+      if (t + 5 < n_tiles) iteration(t + 5, std::integral_constant<int, 2>{}, snB, snA, pwB, pwA);
     }
   }
 
