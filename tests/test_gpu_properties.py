@@ -33,6 +33,21 @@ def test_bitwise_deterministic(cp):
     b = cp.ring_prefill(q, k, v, 4, "pass_kv", True)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    banner("determinism fused")
+    a = cp.ring_prefill_fused(q, k, v, 4, True)
+    b = cp.ring_prefill_fused(q, k, v, 4, True)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    banner("determinism accumulate")
+    runs = []
+    for _ in range(2):
+        o = torch.empty(1, 2048, 8, 128, device=DEV)
+        l = torch.empty(1, 2048, 8, device=DEV)
+        for step in range(4):
+            cp.ring_step_accumulate(q, k, v, 4, step, o, l, "pass_q", True)
+        runs.append((o, l))
+    torch.cuda.synchronize()
+    assert torch.equal(runs[0][0], runs[1][0]) and torch.equal(runs[0][1], runs[1][1])
     qd = si.draw_tensor(4, 0, (8, 1, 16, 128), torch.bfloat16).to(DEV)
     kd = si.draw_tensor(4, 1, (8, 8192, 1, 128), torch.bfloat16).to(DEV)
     vd = si.draw_tensor(4, 2, (8, 8192, 1, 128), torch.bfloat16).to(DEV)
