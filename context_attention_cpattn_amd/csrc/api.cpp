@@ -37,6 +37,8 @@ cpattn_status hip_fail(hipError_t e, const char* what) {
   return fail(CPATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+constexpr int64_t kMaxKvTokenStride = int64_t(1) << 24;
+
 int64_t elem_bytes(int32_t dt) { return dt == CPATTN_BF16 ? 2 : (dt == CPATTN_F32 ? 4 : 0); }
 
 int64_t numel(const cpattn_tensor& t) { return t.B * t.S * t.H * t.D; }
@@ -96,6 +98,9 @@ cpattn_status check_qkv(const cpattn_tensor* q, const cpattn_tensor* k, const cp
   if (q->D != 64 && q->D != 128)
     return fail(CPATTN_ERR_UNSUPPORTED, "head_dim %lld not supported (64 or 128)", (long long)q->D);
   if ((int64_t)q->B * q->H > INT32_MAX / 4) return fail(CPATTN_ERR_UNSUPPORTED, "B*Hq too large");
+  // the prefill kernel addresses a K/V tile by 32-bit byte offsets from its start
+  if (k->stride_s > kMaxKvTokenStride || v->stride_s > kMaxKvTokenStride)
+    return fail(CPATTN_ERR_UNSUPPORTED, "k/v token strides above 2^24 elements are not supported");
   return ok();
 }
 

@@ -74,6 +74,13 @@ __device__ __forceinline__ void gload_lds16(const void* gptr, uint32_t lds_base)
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
                : "memory");
 }
+// The same transfer addressed as a wave-uniform base in SGPRs plus a 32-bit
+// per-lane byte offset (the saddr form): moving the base costs scalar adds
+// only, no vector instructions.
+__device__ __forceinline__ void gload_lds16(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
 }

@@ -386,7 +386,7 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: fetch bases and LDS targets stay scalar
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
@@ -451,20 +451,22 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
     }
     // Fetch: piece i of fetching wave fw, lane l is tile slot i*FW*64 + fw*64 + l,
     // which holds key slot>>4 at physical chunk slot&15 (logical chunk for K:
-    // ^ (key & 15), for V: ^ 4 (key & 3)).  The source pointers advance one
+    // ^ (key & 15), for V: ^ 4 (key & 3)).  Each lane keeps its pieces' byte
+    // offsets from the tile start; the tile starts are scalar and advance one
     // tile per fetch.
     const bool fetcher = wave < FW;
     int fkey[FL];
-    const __bf16* kf[FL];
-    const __bf16* vf[FL];
+    uint32_t kof[FL], vof[FL];
 #pragma unroll
     for (int i = 0; i < FL; ++i) {
       const int slot = i * FW * 64 + (wave % FW) * 64 + lane;
       fkey[i] = slot >> 4;
-      kf[i] = kp + fkey[i] * a.k_ss + (((slot & 15) ^ (fkey[i] & 15)) << 3);
-      vf[i] = vp + fkey[i] * a.v_ss + (((slot & 15) ^ (4 * (fkey[i] & 3))) << 3);
+      kof[i] = (uint32_t)(2 * (fkey[i] * a.k_ss + (((slot & 15) ^ (fkey[i] & 15)) << 3)));
+      vof[i] = (uint32_t)(2 * (fkey[i] * a.v_ss + (((slot & 15) ^ (4 * (fkey[i] & 3))) << 3)));
     }
-    const int64_t kstep = (int64_t)BN * a.k_ss, vstep = (int64_t)BN * a.v_ss;
+    const uint8_t* kt = reinterpret_cast<const uint8_t*>(kp);
+    const uint8_t* vt = reinterpret_cast<const uint8_t*>(vp);
+    const int64_t kstep = 2 * BN * a.k_ss, vstep = 2 * BN * a.v_ss;
     const uint32_t lbase = lds_addr(smem) + (wave % FW) * 64 * 16;
     int n_fetched = 0;
     auto fetch = [&](int stage) {
@@ -473,8 +475,8 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
         if ((n_fetched + 1) * BN <= Sk) {
 #pragma unroll
           for (int i = 0; i < FL; ++i) {
-            gload_lds16(kf[i], dst + i * FW * 64 * 16);
-            gload_lds16(vf[i], dst + i * FW * 64 * 16 + VBASE);
+            gload_lds16(kt, kof[i], dst + i * FW * 64 * 16);
+            gload_lds16(vt, vof[i], dst + i * FW * 64 * 16 + VBASE);
           }
         } else {
           // rows past the block end re-read the last row: their scores are
@@ -482,15 +484,12 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
 #pragma unroll
           for (int i = 0; i < FL; ++i) {
             const int over = max(0, n_fetched * BN + fkey[i] - (Sk - 1));
-            gload_lds16(kf[i] - over * a.k_ss, dst + i * FW * 64 * 16);
-            gload_lds16(vf[i] - over * a.v_ss, dst + i * FW * 64 * 16 + VBASE);
+            gload_lds16(kt, kof[i] - (uint32_t)(2 * over * a.k_ss), dst + i * FW * 64 * 16);
+            gload_lds16(vt, vof[i] - (uint32_t)(2 * over * a.v_ss), dst + i * FW * 64 * 16 + VBASE);
           }
         }
-#pragma unroll
-        for (int i = 0; i < FL; ++i) {
-          kf[i] += kstep;
-          vf[i] += vstep;
-        }
+        kt += kstep;
+        vt += vstep;
       }
       ++n_fetched;
     };
