@@ -29,7 +29,8 @@
  *    A row that sees no key gets LSE = -inf and an all-zero output row.
  *  - Supported: D in {64, 128}; Q/K/V all BF16 (bf16 MFMA, fp32 accumulate)
  *    or all F32 (fp32 vector arithmetic).  Partial outputs and LSE are F32.
- *    Sequence lengths below 2^30; B and H below 2^31.
+ *    Sequence lengths below 2^30; B and H below 2^31; K and V token strides
+ *    (stride_s) of at most 2^24 elements (CPATTN_ERR_UNSUPPORTED beyond).
  *  - Alignment: every data pointer 16-byte aligned; for Q/K/V/O the strides
  *    (stride_b, stride_s, stride_h) are multiples of 16 bytes' worth of
  *    elements (8 for BF16, 4 for F32).  LSE strides are unconstrained.

@@ -98,6 +98,10 @@ def test_partial_validation():
     # batch mismatch, k/v mismatch
     assert call_partial(q, bshd(2, 64, 2, 128), v, out, lse) == cp.ERR_INVALID_ARG
     assert call_partial(q, k, bshd(1, 65, 2, 128), out, lse) == cp.ERR_INVALID_ARG
+    # K/V token strides beyond 2^24 elements
+    wide_k, wide_v = bshd(1, 64, 2, 128), bshd(1, 64, 2, 128)
+    wide_k.stride_s = wide_v.stride_s = (1 << 24) + 8
+    assert call_partial(q, wide_k, wide_v, out, lse) == cp.ERR_UNSUPPORTED and "2^24" in err()
 
 
 @no_gpu
