@@ -490,12 +490,19 @@ def summarize_pmc(fetch_dir: str, write_dir: str, clock_dir: str | None = None, 
             f.write(f"# split-KV decode kernel of the same runs ({nd} dispatches), same calibration\n")
             f.write(f"decode_fetch_bytes_per_launch: {d_f * 1024.0 * f_scale:.0f}\n")
             f.write(f"decode_write_bytes_per_launch: {d_w * 1024.0 * w_scale:.0f}\n")
+        m_f, nm = _per_dispatch(fr, "FETCH_SIZE", "ring_merge_kernel")
+        m_w, _ = _per_dispatch(wr, "WRITE_SIZE", "ring_merge_kernel")
+        if m_f is not None and m_w is not None:
+            f.write(f"# ring merge kernel of the same runs ({nm} dispatch(es), every owner of one Pass-KV step each), "
+                    "same calibration\n")
+            f.write(f"ring_merge_fetch_bytes_per_launch: {m_f * 1024.0 * f_scale:.0f}\n")
+            f.write(f"ring_merge_write_bytes_per_launch: {m_w * 1024.0 * w_scale:.0f}\n")
         if rdreq_dir:
             rr = _pmc_rows(rdreq_dir)
             f.write("# cross-check from a run with TCC_EA0_RDREQ_{,128B_,64B_,32B_}sum: bytes read = 128/64/32 x\n"
                     "# the requests of each size (no calibration; 'other' = requests of none of those sizes)\n")
             for label, part in (("partial", "partial_bf16_d128_kernel"), ("decode", "decode_stream_kernel"),
-                                ("copy", "MulFunctor")):
+                                ("ring_merge", "ring_merge_kernel"), ("copy", "MulFunctor")):
                 rb, other = _read_bytes_by_size(rr, part)
                 if rb is not None:
                     f.write(f"{label}_read_bytes_by_request_size: {rb:.0f} (other requests: {other:.0f})\n")
