@@ -1,0 +1,68 @@
+"""Host-side logic of bench.py (no GPU): the one-GPU guard, the per-step FLOP
+count, and the rocprofv3 counter summary that feeds the roofline's traffic,
+clock and MFMA-busy figures."""
+import csv
+import os
+
+import pytest
+
+import bench
+import seeded_inputs as si
+
+
+def test_more_than_one_gpu_is_refused(capsys):
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU" in capsys.readouterr().err
+
+
+@pytest.mark.parametrize("name", ["prefill_bf16_s128k_p16", "gqa16_bf16_s8k_p8", "prefill_bf16_s1m_p8"])
+@pytest.mark.parametrize("order", ["pass_kv", "pass_q"])
+def test_ring_step_flops_cover_the_causal_triangle(name, order):
+    w = si.WORKLOADS[name]
+    steps = bench.ring_step_flops(w, order)
+    assert len(steps) == w.n_chunks
+    # S(S+1)/2 visible pairs at 4 * D * Hq FLOP each, split over the steps
+    assert sum(steps) == pytest.approx(4.0 * w.D * w.Hq * w.B * w.Sq * (w.Sq + 1) / 2, rel=1e-12)
+    assert sum(steps) == pytest.approx(w.flops(), rel=1e-12)
+    # step 0 holds the P diagonal pairs (half a full pair each, plus the diagonal itself)
+    C = w.chunk
+    assert steps[0] == pytest.approx(w.n_chunks * 4.0 * w.D * w.Hq * w.B * C * (C + 1) / 2, rel=1e-12)
+
+
+def _write_counters(d, rows):
+    os.makedirs(d, exist_ok=True)
+    fields = ["Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    with open(os.path.join(d, "p_counter_collection.csv"), "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=fields)
+        wr.writeheader()
+        for r in rows:
+            wr.writerow(dict(zip(fields, r)))
+
+
+def test_counter_summary_scales_by_the_copy_kernel(tmp_path, monkeypatch):
+    out = tmp_path / "traffic.txt"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
+    k, copy = "partial_bf16_d128_kernel(args)", "vectorized_elementwise_kernel<MulFunctor>"
+    gib_kib = (1 << 30) / 1024.0
+    # the copy kernel's FETCH_SIZE reads half its true bytes (scale 2), WRITE_SIZE all of them
+    _write_counters(tmp_path / "f", [(k, "FETCH_SIZE", 1000.0, 0, 1), (k, "FETCH_SIZE", 3000.0, 0, 1),
+                                     (copy, "FETCH_SIZE", gib_kib / 2, 0, 1)])
+    _write_counters(tmp_path / "w", [(k, "WRITE_SIZE", 500.0, 0, 1), (k, "WRITE_SIZE", 500.0, 0, 1),
+                                     (copy, "WRITE_SIZE", gib_kib, 0, 1)])
+    # 8 XCDs x 1.6 GHz over a 1 ms dispatch; the copy at 2.4 GHz
+    _write_counters(tmp_path / "c", [(k, "GRBM_GUI_ACTIVE", 8 * 1.6e6, 0, 1_000_000),
+                                     (copy, "GRBM_GUI_ACTIVE", 8 * 2.4e6, 0, 1_000_000)])
+    assert bench.summarize_pmc(str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "c")) == 0
+    kv = dict(ln.split(":", 1) for ln in out.read_text().splitlines() if ":" in ln and not ln.startswith("#"))
+    assert float(kv["copy_fetch_scale"]) == pytest.approx(2.0)
+    assert float(kv["copy_write_scale"]) == pytest.approx(1.0)
+    assert float(kv["fetch_bytes_per_launch"]) == pytest.approx(2000.0 * 1024 * 2.0)
+    assert float(kv["write_bytes_per_launch"]) == pytest.approx(500.0 * 1024)
+    assert float(kv["hbm_bytes_per_launch"]) == pytest.approx(2000.0 * 2048 + 500.0 * 1024)
+    assert float(kv["sclk_ghz_partial_kernel"]) == pytest.approx(1.6)
+    assert float(kv["sclk_ghz_copy_kernel"]) == pytest.approx(2.4)
+    # the bench reads it back only while the kernel source is the one the counters were taken on
+    hbm, clk, _, _ = bench.read_pmc_summary()
+    assert hbm == pytest.approx(2000.0 * 2048 + 500.0 * 1024) and clk == pytest.approx(1.6)
+    out.write_text(out.read_text().replace(bench.kernel_hash(), "0" * 16))
+    assert bench.read_pmc_summary() == (None, None, None, None)
