@@ -51,7 +51,7 @@ def log(*a):
 
 def kernel_hash() -> str:
     h = hashlib.sha256()
-    for name in ("partial_bf16.hip", "device.h", "internal.h"):
+    for name in ("partial_bf16.hip", "decode.hip", "merge.hip", "device.h", "internal.h"):
         with open(os.path.join(ROOT, "context_attention_cpattn_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -74,26 +74,33 @@ def ring_step_flops(w, order: str):
     return out
 
 
-def read_pmc_summary():
-    """(HBM bytes per launch, shader clock GHz, MFMA busy fraction) of the partial kernel from the
-    committed pmc summary, each None if absent or if the kernel source changed since it was taken."""
+def pmc_values() -> dict:
+    """Numeric entries of the committed pmc summary; empty if it is absent or if a kernel source
+    changed since the counters were taken."""
     if not os.path.exists(TRAFFIC_FILE):
-        return None, None, None, None
+        return {}
     kv = {}
     for ln in open(TRAFFIC_FILE):
         if ":" in ln and not ln.startswith("#"):
             a, b = ln.split(":", 1)
             kv[a.strip()] = b.strip()
     if kv.get("kernel_source_sha256_16") != kernel_hash():
-        return None, None, None, None
-
-    def num(key):
+        return {}
+    out = {}
+    for key, val in kv.items():
         try:
-            return float(kv[key])
-        except (KeyError, ValueError):
-            return None
-    return (num("hbm_bytes_per_launch"), num("sclk_ghz_partial_kernel"), num("mfma_busy_fraction"),
-            num("frac_of_peak_at_measured_sclk"))
+            out[key] = float(val.split()[0])
+        except (ValueError, IndexError):
+            pass
+    return out
+
+
+def read_pmc_summary():
+    """(HBM bytes per launch, shader clock GHz, MFMA busy fraction, fraction of peak at that clock)
+    of the partial kernel from the committed pmc summary, each None when unavailable."""
+    kv = pmc_values()
+    return (kv.get("hbm_bytes_per_launch"), kv.get("sclk_ghz_partial_kernel"), kv.get("mfma_busy_fraction"),
+            kv.get("frac_of_peak_at_measured_sclk"))
 
 
 def cpu_baseline(w, q, k, v, seconds: float):
@@ -384,6 +391,12 @@ def main(argv=None) -> int:
         gbs = dec_bytes / (ms * 1e-3) / 1e9
         result["decode"] = {"workload": wd.name, "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
                             "ms": round(ms, 4), "algorithmic_bytes": dec_bytes, "peak_GB/s": PEAK_HBM_GBS}
+        pmc = pmc_values()
+        if "decode_fetch_bytes_per_launch" in pmc and "decode_write_bytes_per_launch" in pmc:
+            # HBM bytes the decode kernel itself moved per call (counters, copy-calibrated; the
+            # 8-way merge after it is not included), from the committed summary of this source
+            result["decode"]["kernel_traffic_profiled"] = pmc["decode_fetch_bytes_per_launch"] + \
+                pmc["decode_write_bytes_per_launch"]
         log(f"[bench] decode {ms:.3f} ms, {gbs:.0f} GB/s")
         del dq, dk, dv, dws
 
