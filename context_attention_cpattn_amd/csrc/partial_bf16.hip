@@ -319,7 +319,9 @@ __global__ __launch_bounds__(256) void partial_bf16_kernel(const PartialLaunch a
 // LDS: the K tiles of the three stages (64 keys x 256 B each, 16-byte chunks
 // XOR-swizzled by key & 15), then their V tiles (chunks XOR-swizzled by
 // 4 (key & 3)); with K and V apart, every operand read reaches its data
-// through the 16-bit offset of ds_read from one per-lane base.
+// through the 16-bit offset of ds_read from one per-lane base.  The query
+// tile (256 rows x 256 B) has a 64 KB region of its own, filled once per
+// workgroup, for 160 KB in all.
 //
 // Each wave's work is software-pipelined so that its matrix and vector work
 // overlap.  Iteration t runs two phases:
@@ -383,6 +385,7 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
   constexpr int FL = 1024 / (FW * 64);  // 16-byte pieces of K (and of V) per fetching lane
   constexpr float SCALE_LOG2 = 0.12751743082459868f;  // log2(e) / sqrt(128)
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * NST * TBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t qsm[BM * D * 2];  // the query tile, rows of 256 B
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -432,10 +435,19 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
   if (n_tiles > 0) {
     bf16x8 qf[NDS];
     {
-      const __bf16* qr = qp + (int64_t)row * a.q_ss + 8 * g;
-      const bool ok = row < a.Sq;
+      // The query tile reaches LDS by whole rows (16 lanes per 256-byte row, 16-byte
+      // chunks XOR-swizzled by the row), so each load moves four contiguous row
+      // pieces instead of 32 scattered ones; rows past the block end re-read its
+      // last row and are zeroed when read back.
+      const uint32_t qdst = lds_addr(qsm) + wave * 64 * 16;
 #pragma unroll
-      for (int s2 = 0; s2 < NDS; ++s2) qf[s2] = ok ? as_bf16x8(ld_global16(qr + 16 * s2)) : (bf16x8){};
+      for (int i = 0; i < 8; ++i) {
+        const int slot = i * 512 + wave * 64 + lane;
+        const int rr = slot >> 4;
+        const int c = (slot & 15) ^ (rr & 15);
+        const int grow = min(m0 + rr, a.Sq - 1);
+        gload_lds16(qp + (int64_t)grow * a.q_ss + c * 8, qdst + i * 512 * 16);
+      }
     }
     // K operand of k-step s: row l32 (+32 for key block 1), chunk 2s+g swizzled by the row
     int koff[NDS];
@@ -560,6 +572,15 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
     for (int i = 0; i < NST - 1; ++i)
       if (i < n_tiles) fetch(i);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    {
+      // Q fragments, B operand of S^T = K Q^T: column = this lane's row,
+      // k-slots = d in [16 s + 8 g, 16 s + 8 g + 8)
+      const int rr = wave * 32 + l32;
+      const bool ok = row < a.Sq;
+#pragma unroll
+      for (int s2 = 0; s2 < NDS; ++s2)
+        qf[s2] = ok ? as_bf16x8(ld_lds16(qsm + rr * 256 + (((2 * s2 + g) ^ (rr & 15)) << 4))) : (bf16x8){};
+    }
     {
       scores(smem, snA);
       mask_tile(snA, 0);
