@@ -372,6 +372,7 @@ __device__ __forceinline__ void pin(T& x) {
   asm volatile("" : "+v"(x));
 }
 
+template <bool SEG>
 __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLaunch a, const int n_qtiles) {
   constexpr int D = 128, BN = 64, NDS = 8, BM = 256;
   constexpr int TBYTES = BN * D * 2;  // one K or V tile
@@ -431,6 +432,32 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
   for (int db = 0; db < 4; ++db) o[db] = (f32x16){};
   float m = kNegInf;  // running reference (log2 domain) of this lane's row
   float l = 0.f;      // this lane's share of the row sum, relative to m
+
+  // normalise and store this lane's row of segment `seg` (slot item.slot + seg)
+  auto write_out = [&](int seg) {
+    const float l_tot = pair32_sum(l);
+    if (row < a.Sq) {
+      const bool acc = a.accumulate != 0;
+      float* const lps = lp != nullptr ? lp + seg * a.l_slot : nullptr;
+      const RowOut ro = row_out(m, l_tot, acc, acc ? lps[(int64_t)row * a.l_ss] : 0.f);
+      float* orow = op + seg * a.o_slot + (int64_t)row * a.o_ss;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          float* dst = orow + db * 32 + 8 * i4 + 4 * g;
+          f32x4 v4 = {o[db][4 * i4 + 0] * ro.s_new, o[db][4 * i4 + 1] * ro.s_new, o[db][4 * i4 + 2] * ro.s_new,
+                      o[db][4 * i4 + 3] * ro.s_new};
+          if (acc) {
+            const f32x4 old = *reinterpret_cast<const f32x4*>(dst);
+            v4 = (f32x4){fmaf(old[0], ro.s_old, v4[0]), fmaf(old[1], ro.s_old, v4[1]), fmaf(old[2], ro.s_old, v4[2]),
+                         fmaf(old[3], ro.s_old, v4[3])};
+          }
+          *reinterpret_cast<f32x4*>(dst) = v4;
+        }
+      if (g == 0 && lps != nullptr) lps[(int64_t)row * a.l_ss] = ro.lse;
+    }
+  };
 
   if (n_tiles > 0) {
     bf16x8 qf[NDS];
@@ -699,6 +726,28 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
       }
       lt += pp;
       pn[7] = pack_bf16(pe, pp);
+      if constexpr (SEG) {
+        if ((t + 1) % a.seg_tiles == 0 && t + 1 < n_tiles) {
+          // A chunk boundary: this pair's partial is complete, and the next
+          // pair starts exactly as a launch of its own would: zero state, the
+          // reference at the row max of its first tile (whose scores x already
+          // holds, masked), then key block 0 of that tile's P.
+          write_out(t / a.seg_tiles);
+#pragma unroll
+          for (int db = 0; db < 4; ++db) o[db] = (f32x16){};
+          m = kNegInf;
+          l = 0.f;
+          lt = 0.f;
+          move_to_max(x);
+          need = false;
+#pragma unroll
+          for (int w = 0; w < 8; ++w) {
+            const float p0 = prob(x[0][2 * w]);
+            const float p1 = prob(x[0][2 * w + 1]);
+            pn[w] = pack_bf16(p0, p1);
+          }
+        }
+      }
       STAMP(wave, t, 2, L);
       // tile t+2 (fetched above) must have landed before any wave reads it
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -716,27 +765,7 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
     }
   }
 
-  const float l_tot = pair32_sum(l);
-  if (row < a.Sq) {
-    const bool acc = a.accumulate != 0;
-    const RowOut ro = row_out(m, l_tot, acc, acc ? lp[(int64_t)row * a.l_ss] : 0.f);
-    float* orow = op + (int64_t)row * a.o_ss;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        float* dst = orow + db * 32 + 8 * i4 + 4 * g;
-        f32x4 v4 = {o[db][4 * i4 + 0] * ro.s_new, o[db][4 * i4 + 1] * ro.s_new, o[db][4 * i4 + 2] * ro.s_new,
-                    o[db][4 * i4 + 3] * ro.s_new};
-        if (acc) {
-          const f32x4 old = *reinterpret_cast<const f32x4*>(dst);
-          v4 = (f32x4){fmaf(old[0], ro.s_old, v4[0]), fmaf(old[1], ro.s_old, v4[1]), fmaf(old[2], ro.s_old, v4[2]),
-                       fmaf(old[3], ro.s_old, v4[3])};
-        }
-        *reinterpret_cast<f32x4*>(dst) = v4;
-      }
-    if (g == 0 && lp != nullptr) lp[(int64_t)row * a.l_ss] = ro.lse;
-  }
+  write_out(SEG && n_tiles > 0 ? (n_tiles - 1) / a.seg_tiles : 0);
 }
 
 }  // namespace
@@ -747,8 +776,10 @@ hipError_t launch_partial_bf16(const PartialLaunch& a, int D, int n_qtiles, hipS
   const long long blocks = (long long)a.n_items * a.B * a.Hq * n_qtiles;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  if (D == 128)
-    hipLaunchKernelGGL(partial_bf16_d128_kernel, dim3((unsigned)blocks), dim3(512), 0, s, a, n_qtiles);
+  if (D == 128 && a.seg_tiles > 0)
+    hipLaunchKernelGGL(partial_bf16_d128_kernel<true>, dim3((unsigned)blocks), dim3(512), 0, s, a, n_qtiles);
+  else if (D == 128)
+    hipLaunchKernelGGL(partial_bf16_d128_kernel<false>, dim3((unsigned)blocks), dim3(512), 0, s, a, n_qtiles);
   else if (D == 64)
     hipLaunchKernelGGL(partial_bf16_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, s, a, n_qtiles);
   else

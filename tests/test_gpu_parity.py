@@ -154,12 +154,16 @@ def test_ring_small_orders(cp, P, order, causal):
     assert torch.equal(o16.cpu(), o.cpu().to(torch.bfloat16))
 
 
-@pytest.mark.parametrize("P,order,causal", [(4, "pass_kv", True), (4, "pass_q", True), (3, "pass_kv", False),
-                                            (3, "pass_q", False), (9, "pass_kv", True)])
-def test_ring_merge_follows_arrival_order(cp, P, order, causal):
+@pytest.mark.parametrize("P,order,causal,C", [(4, "pass_kv", True, 96), (4, "pass_q", True, 96), (3, "pass_kv", False, 96),
+                                              (3, "pass_q", False, 96), (9, "pass_kv", True, 96),
+                                              (4, "pass_kv", True, 128), (3, "pass_q", False, 192),
+                                              (5, "pass_q", True, 320)])
+def test_ring_merge_follows_arrival_order(cp, P, order, causal, C):
     """The ring driver's merge equals, bit for bit, merging the same partials in the
-    arrival order the oracle's schedule defines (partials via the partial entry point)."""
-    C, H, D = 96, 2, 128
+    arrival order the oracle's schedule defines (partials via the partial entry point).
+    Chunks of a multiple of 64 tokens take the driver's one-walk-per-owner launch, whose
+    partials must be those of the per-pair launches bit for bit."""
+    H, D = 2, 128
     S = C * P
     q = draw(61 + P, (1, S, H, D), torch.bfloat16, 0).to(DEV)
     k = draw(61 + P, (1, S, 1, D), torch.bfloat16, 1).to(DEV)
