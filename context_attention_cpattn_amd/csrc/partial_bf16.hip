@@ -372,6 +372,10 @@ __device__ __forceinline__ void pin(T& x) {
   asm volatile("" : "+v"(x));
 }
 
+// SEG: an item's key range is a run of chunks of seg_tiles tiles each, and
+// every chunk's partial goes to its own slot (item.slot + chunk): at each
+// boundary the finished partial is written and the softmax restarts exactly as
+// a launch of that chunk alone would.  Without SEG an item writes one result.
 template <bool SEG>
 __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLaunch a, const int n_qtiles) {
   constexpr int D = 128, BN = 64, NDS = 8, BM = 256;
