@@ -325,7 +325,8 @@ def main(argv=None) -> int:
                            "launch": "ring_prefill_fused: each owner's visible keys in one pass, no merge"}
 
     def prefill_leg(name: str, reps: int):
-        """Median time of whole Pass-KV ring prefills of another workload (2 warm-ups)."""
+        """Median time of whole Pass-KV ring prefills of another workload, timed back to back after
+        a warm-up of at least two calls and ~50 ms (the GPU idled while the inputs were drawn)."""
         wx = si.WORKLOADS[name]
         log(f"[bench] drawing {wx.name} inputs")
         xq_, xk_, xv_ = si.make_qkv(wx)
@@ -335,16 +336,27 @@ def main(argv=None) -> int:
                           device=dev)
         xout = torch.empty(wx.q_shape(), dtype=torch.float32, device=dev)
         xlse = torch.empty(wx.q_shape()[:3], dtype=torch.float32, device=dev)
-        for _ in range(2):
+        def run():
             cp.ring_prefill(xq, xk, xv, wx.n_chunks, "pass_kv", True, out=xout, lse=xlse, workspace=xws)
+
+        for _ in range(2):
+            run()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run()
+        e1.record(stream)
         torch.cuda.synchronize()
+        for _ in range(min(200, int(50.0 / max(e0.elapsed_time(e1), 1e-3)))):
+            run()
         evx = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
         for i in range(reps):
             evx[i][0].record(stream)
-            cp.ring_prefill(xq, xk, xv, wx.n_chunks, "pass_kv", True, out=xout, lse=xlse, workspace=xws)
+            run()
             evx[i][1].record(stream)
-            torch.cuda.synchronize()
-            log(f"[bench] {wx.name} rep {i + 1}/{reps}: {evx[i][0].elapsed_time(evx[i][1]):.3f} ms")
+            if wx.flops() > 1e15:  # long calls: report progress as they finish
+                torch.cuda.synchronize()
+                log(f"[bench] {wx.name} rep {i + 1}/{reps}: {evx[i][0].elapsed_time(evx[i][1]):.3f} ms")
+        torch.cuda.synchronize()
         msx = sorted(e[0].elapsed_time(e[1]) for e in evx)[reps // 2]
         tf = wx.flops() / (msx * 1e-3) / 1e12
         del xws
