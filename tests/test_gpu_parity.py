@@ -157,7 +157,7 @@ def test_ring_small_orders(cp, P, order, causal):
 @pytest.mark.parametrize("P,order,causal,C", [(4, "pass_kv", True, 96), (4, "pass_q", True, 96), (3, "pass_kv", False, 96),
                                               (3, "pass_q", False, 96), (9, "pass_kv", True, 96),
                                               (4, "pass_kv", True, 128), (3, "pass_q", False, 192),
-                                              (5, "pass_q", True, 320)])
+                                              (5, "pass_q", True, 320), (6, "pass_kv", True, 64)])
 def test_ring_merge_follows_arrival_order(cp, P, order, causal, C):
     """The ring driver's merge equals, bit for bit, merging the same partials in the
     arrival order the oracle's schedule defines (partials via the partial entry point).
@@ -178,6 +178,23 @@ def test_ring_merge_follows_arrival_order(cp, P, order, causal, C):
         torch.cuda.synchronize()
         assert torch.equal(om, o[:, i * C:(i + 1) * C]), f"owner {i}: O differs"
         assert torch.equal(lm, l[:, i * C:(i + 1) * C]), f"owner {i}: LSE differs"
+
+
+@pytest.mark.parametrize("P,C,B,Hkv,order,causal", [(64, 64, 1, 1, "pass_kv", True), (8, 64, 2, 2, "pass_q", False),
+                                                   (4, 320, 2, 2, "pass_kv", True), (3, 4096, 1, 1, "pass_q", True)])
+def test_ring_prefill_chunk_walk(cp, P, C, B, Hkv, order, causal):
+    """Chunks of a multiple of 64 tokens (up to 4096): the driver's per-owner walk that writes every
+    pair's partial at the chunk boundary, against the oracle; 64-token chunks put a boundary after
+    every tile, and the last case has chunks of the limit's length."""
+    S, H = C * P, 4
+    q = draw(131 + P, (B, S, H, 128), torch.bfloat16, 0)
+    k = draw(131 + P, (B, S, Hkv, 128), torch.bfloat16, 1)
+    v = draw(131 + P, (B, S, Hkv, 128), torch.bfloat16, 2)
+    o_ref, l_ref = oracle.full_attention(q, k, v, causal)
+    banner("ring chunk walk", P, C, B, Hkv, order, causal)
+    o, l = cp.ring_prefill(q.to(DEV), k.to(DEV), v.to(DEV), P, order, causal)
+    torch.cuda.synchronize()
+    compare(o, l, o_ref, l_ref, BF16_TOL, f"ring chunk walk P={P} C={C} B={B} Hkv={Hkv} {order} causal={causal}")
 
 
 @pytest.mark.parametrize("P,order,causal,D,dtype", [(1, "pass_kv", True, 128, "bf16"), (4, "pass_kv", True, 128, "bf16"),
