@@ -13,6 +13,7 @@
 // MFMA: S^T = K Q^T puts keys on rows, so a lane holds 4 keys of one head and
 // the row max / sum are reduced across the 4 lane groups.
 #include <algorithm>
+#include <atomic>
 
 #include "device.h"
 #include "internal.h"
@@ -302,23 +303,35 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeLaunch a
 
 }  // namespace
 
+// Compute units of the current device, cached per device.  Several host
+// threads may make their first call at once: each entry is an atomic that
+// they may all fill with the same value.
+hipError_t cu_count(int* out) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    n = n > 0 ? n : 1;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  *out = n;
+  return hipSuccess;
+}
+
 hipError_t launch_decode_bf16(const DecodeLaunch& a, int D, hipStream_t s) {
   const long long units = (long long)a.B * a.Hkv * a.head_blocks * a.n_chunks * a.n_split;
   if (units <= 0) return hipSuccess;
   if (units > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   // one persistent workgroup per CU (the LDS stages take most of a CU's LDS)
-  static int n_cu[64] = {0};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  int n_cu = 0;
+  const hipError_t e = cu_count(&n_cu);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (n_cu[dev] == 0) {
-    int n = 0;
-    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    n_cu[dev] = n > 0 ? n : 1;
-  }
-  const int grid = (int)std::min<long long>(units, n_cu[dev]);
+  const int grid = (int)std::min<long long>(units, n_cu);
   if (D == 128)
     hipLaunchKernelGGL(decode_stream_kernel<128>, dim3(grid), dim3(256), 0, s, a, (int)units);
   else if (D == 64)

@@ -99,6 +99,8 @@ hipError_t launch_merge(const MergeLaunch& a, hipStream_t s);
 hipError_t launch_ring_merge(const RingMergeLaunch& a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeLaunch& a, int D, hipStream_t s);
 
+hipError_t cu_count(int* out);  // compute units of the current device (cached, thread-safe)
+
 int partial_bf16_rows_per_block(int D);  // query rows per workgroup of the bf16 kernel
 int partial_f32_rows_per_block(int D);
 

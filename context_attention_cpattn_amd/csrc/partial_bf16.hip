@@ -29,12 +29,6 @@
 
 namespace cpattn {
 namespace {
-#ifdef CPATTN_TIMING
-__device__ unsigned long long g_cpattn_stamps[8 * 160 * 4];
-#define STAMP(w, p, k, blk) do { if ((blk) == CPATTN_TIMING && (p) < 160 && (threadIdx.x & 63) == 0) g_cpattn_stamps[((w) * 160 + (p)) * 4 + (k)] = __builtin_readcyclecounter(); } while (0)
-#else
-#define STAMP(w, p, k, blk) do {} while (0)
-#endif
 
 constexpr float kTau = 8.0f;
 constexpr float kTwoTau = 256.0f;  // 2^kTau
@@ -636,7 +630,6 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
       constexpr int SL = (ST + NST - 1) % NST;
       const uint8_t* cur = smem + ST * TBYTES;  // K of tile t at cur, V at cur + VBASE (voff)
       const uint8_t* nxt = smem + SN * TBYTES;
-      STAMP(wave, t, 0, L);
       // tile t+2 goes into the stage tile t-1 used
       const bool do_fetch = t + NST - 1 < n_tiles;
       if (do_fetch) fetch(SL);
@@ -691,7 +684,6 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
       l += lt;
       lt = 0.f;
       __builtin_amdgcn_sched_barrier(0);
-      STAMP(wave, t, 1, L);
 
       // ---- phase B: O^T += V(t)^T P(t)^T; key block 0 of P(t+1) ----
       __builtin_amdgcn_s_setprio(0);
@@ -752,10 +744,8 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
           }
         }
       }
-      STAMP(wave, t, 2, L);
       // tile t+2 (fetched above) must have landed before any wave reads it
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      STAMP(wave, t, 3, L);
     };
     // six iterations per trip: three LDS stages times two register sets
     static_assert(NST == 3, "the loop below is unrolled over three stages");
@@ -793,9 +783,3 @@ hipError_t launch_partial_bf16(const PartialLaunch& a, int D, int n_qtiles, hipS
 
 }  // namespace cpattn
 
-#ifdef CPATTN_TIMING
-extern "C" int cpattn_debug_stamps(unsigned long long* host, int n) {
-  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(cpattn::g_cpattn_stamps), sizeof(unsigned long long) * n, 0,
-                                  hipMemcpyDeviceToHost);
-}
-#endif
