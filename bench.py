@@ -181,7 +181,7 @@ def main(argv=None) -> int:
     q, k, v = si.make_qkv(w)
     gq, gk, gv = q.to(dev), k.to(dev), v.to(dev)
     P = w.n_chunks
-    ws = torch.empty(cp.ring_prefill_workspace_size(gq, P, args.order, True), dtype=torch.uint8, device=dev)
+    ws = torch.empty(cp.ring_prefill_workspace_size(gq, P, True), dtype=torch.uint8, device=dev)
     out = torch.empty(w.q_shape(), dtype=torch.float32, device=dev)
     lse = torch.empty(w.q_shape()[:3], dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -266,7 +266,7 @@ def main(argv=None) -> int:
     # the other ring order of the same prefill, as whole ring prefills (all pairs in one launch)
     if not args.no_other_order:
         other = "pass_q" if args.order == "pass_kv" else "pass_kv"
-        ws2 = torch.empty(cp.ring_prefill_workspace_size(gq, P, other, True), dtype=torch.uint8, device=dev)
+        ws2 = torch.empty(cp.ring_prefill_workspace_size(gq, P, True), dtype=torch.uint8, device=dev)
         cp.ring_prefill(gq, gk, gv, P, other, True, out=out, lse=lse, workspace=ws2)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -332,7 +332,7 @@ def main(argv=None) -> int:
         xq_, xk_, xv_ = si.make_qkv(wx)
         xq, xk, xv = xq_.to(dev), xk_.to(dev), xv_.to(dev)
         del xq_, xk_, xv_
-        xws = torch.empty(cp.ring_prefill_workspace_size(xq, wx.n_chunks, "pass_kv", True), dtype=torch.uint8,
+        xws = torch.empty(cp.ring_prefill_workspace_size(xq, wx.n_chunks, True), dtype=torch.uint8,
                           device=dev)
         xout = torch.empty(wx.q_shape(), dtype=torch.float32, device=dev)
         xlse = torch.empty(wx.q_shape()[:3], dtype=torch.float32, device=dev)

@@ -129,85 +129,134 @@ hipError_t launch_partial(const cpattn::PartialLaunch& a, int dtype, int D, int 
   return cpattn::launch_partial_f32(a, D, (Sq + rpb - 1) / rpb, st);
 }
 
-// ---- ring schedule (host side; one GPU runs every rank)
-struct Pair {
-  int q, kv;
+// ---- ring layout (host side; one GPU runs every rank)
+//
+// Q [B, Sq, Hq, D] and K/V [B, Skv, Hkv, D] are cut into P equal chunks: Q
+// chunk i has Cq = Sq / P rows at global positions q0 + i Cq + [0, Cq) with
+// q0 = Skv - Sq (the queries are the last Sq positions of the sequence, which
+// makes Sq = Skv the full prefill); K/V chunk j has Ckv = Skv / P rows at
+// j Ckv + [0, Ckv).  Under the causal mask Q chunk i sees the K/V chunks
+// [0, n_vis[i]): those whose first key is not after its last query.  The
+// workspace holds one slot per visible pair, slot0[i] + j.
+struct RingLayout {
+  int P;
+  int64_t Cq, Ckv, q0;
+  int64_t n_items, slot_o, slot_l;  // slots; elements per O slot / LSE slot
+  int32_t n_vis[cpattn::kMaxMerge], slot0[cpattn::kMaxMerge];
+  size_t o_bytes, bytes;
 };
-
-// Work items of ring step s: rank r holds (Q_r, KV_{(r-s) mod P}) under
-// Pass-KV and (Q_{(r-s) mod P}, KV_r) under Pass-Q; causally empty pairs
-// (kv chunk after the q chunk) are dropped.
-std::vector<Pair> ring_step(int P, int s, int order, bool causal) {
-  std::vector<Pair> items;
-  for (int r = 0; r < P; ++r) {
-    const int other = ((r - s) % P + P) % P;
-    Pair p = (order == CPATTN_PASS_KV) ? Pair{r, other} : Pair{other, r};
-    if (causal && p.kv > p.q) continue;
-    items.push_back(p);
-  }
-  return items;
-}
-
-int64_t ring_slot(int P, int i, int j, bool causal) {
-  return causal ? (int64_t)i * (i + 1) / 2 + j : (int64_t)i * P + j;
-}
-
-int64_t ring_items(int P, bool causal) { return causal ? (int64_t)P * (P + 1) / 2 : (int64_t)P * P; }
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-struct RingLayout {
-  int64_t C, n_items, slot_o, slot_l;  // elements per O slot / LSE slot
-  size_t o_bytes, bytes;
-};
-
-RingLayout ring_layout(const cpattn_tensor& q, int P, bool causal) {
+RingLayout ring_layout(const cpattn_tensor& q, int64_t Skv, int P, bool causal) {
   RingLayout L;
-  L.C = q.S / P;
-  L.n_items = ring_items(P, causal);
-  L.slot_o = q.B * L.C * q.H * q.D;
-  L.slot_l = q.B * L.C * q.H;
+  std::memset(&L, 0, sizeof L);
+  L.P = P;
+  L.Cq = q.S / P;
+  L.Ckv = Skv / P;
+  L.q0 = Skv - q.S;
+  for (int i = 0; i < P; ++i) {
+    int64_t n = P;
+    if (L.Cq == 0) n = 0;
+    else if (causal) n = std::min<int64_t>(P, (L.q0 + (i + 1) * L.Cq - 1) / L.Ckv + 1);
+    L.n_vis[i] = (int32_t)n;
+    L.slot0[i] = (int32_t)L.n_items;
+    L.n_items += n;
+  }
+  L.slot_o = q.B * L.Cq * q.H * q.D;
+  L.slot_l = q.B * L.Cq * q.H;
   L.o_bytes = align_up((size_t)(L.n_items * L.slot_o) * 4);
   L.bytes = L.o_bytes + align_up((size_t)(L.n_items * L.slot_l) * 4);
   return L;
 }
 
+struct Pair {
+  int q, kv;
+};
+
+// Work items of ring step s: rank r holds (Q_r, KV_{(r-s) mod P}) under
+// Pass-KV and (Q_{(r-s) mod P}, KV_r) under Pass-Q; pairs whose K/V chunk the
+// Q chunk sees nothing of are dropped.
+std::vector<Pair> ring_step(const RingLayout& L, int s, int order) {
+  std::vector<Pair> items;
+  const int P = L.P;
+  for (int r = 0; r < P; ++r) {
+    const int other = ((r - s) % P + P) % P;
+    const Pair p = (order == CPATTN_PASS_KV) ? Pair{r, other} : Pair{other, r};
+    if (p.kv >= L.n_vis[p.q]) continue;
+    items.push_back(p);
+  }
+  return items;
+}
+
+// Bytes a P-rank ring would move between ranks.  At every step after the
+// first each rank receives its neighbour's chunk: K and V of one chunk under
+// Pass-KV, one Q chunk under Pass-Q.  Under Pass-Q every pair computed away
+// from its Q chunk's owner (all visible pairs but the P diagonal ones) also
+// sends its partial back: fp32 O and fp32 LSE per query row and head.
+struct RingBytes {
+  uint64_t pass_kv, pass_q;
+};
+
+RingBytes ring_bytes(const cpattn_tensor& q, const cpattn_tensor& k, const RingLayout& L) {
+  const uint64_t e = (uint64_t)elem_bytes(q.dtype);
+  const uint64_t hops = (uint64_t)L.P * (uint64_t)(L.P - 1);
+  const uint64_t kv_chunk = 2 * (uint64_t)q.B * L.Ckv * k.H * q.D * e;
+  const uint64_t q_chunk = (uint64_t)q.B * L.Cq * q.H * q.D * e;
+  const uint64_t partial = (uint64_t)q.B * L.Cq * q.H * (q.D + 1) * 4;
+  const uint64_t remote = L.n_items > L.P ? (uint64_t)(L.n_items - L.P) : 0;
+  return RingBytes{hops * kv_chunk, hops * q_chunk + remote * partial};
+}
+
+// CPATTN_ORDER_AUTO: the order that moves fewer bytes, Pass-KV on a tie.
+int resolve_order(int order, const cpattn_tensor& q, const cpattn_tensor& k, const RingLayout& L) {
+  if (order != CPATTN_ORDER_AUTO) return order;
+  const RingBytes rb = ring_bytes(q, k, L);
+  return rb.pass_q < rb.pass_kv ? CPATTN_PASS_Q : CPATTN_PASS_KV;
+}
+
+bool valid_order(int order) { return order == CPATTN_PASS_KV || order == CPATTN_PASS_Q || order == CPATTN_ORDER_AUTO; }
+
 cpattn_status check_ring(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v, int n_chunks,
                          int order, int causal) {
   cpattn_status s;
   if ((s = check_qkv(q, k, v)) != CPATTN_OK) return s;
-  if (k->S != q->S) return fail(CPATTN_ERR_INVALID_ARG, "ring prefill needs k/v of the same length as q");
+  if (k->S < q->S)
+    return fail(CPATTN_ERR_INVALID_ARG, "k/v (%lld rows) must be at least as long as q (%lld rows): the queries are "
+                "the last positions of the sequence", (long long)k->S, (long long)q->S);
   if (n_chunks < 1) return fail(CPATTN_ERR_INVALID_ARG, "n_chunks must be >= 1");
   if (n_chunks > cpattn::kMaxMerge)
     return fail(CPATTN_ERR_UNSUPPORTED, "n_chunks above %d not supported", cpattn::kMaxMerge);
-  if (q->S % n_chunks != 0)
-    return fail(CPATTN_ERR_INVALID_ARG, "sequence length %lld not divisible by n_chunks %d", (long long)q->S, n_chunks);
-  if (order != CPATTN_PASS_KV && order != CPATTN_PASS_Q) return fail(CPATTN_ERR_INVALID_ARG, "unknown ring order");
+  if (q->S % n_chunks != 0 || k->S % n_chunks != 0)
+    return fail(CPATTN_ERR_INVALID_ARG, "sequence lengths %lld (q) and %lld (k/v) must both be divisible by n_chunks %d",
+                (long long)q->S, (long long)k->S, n_chunks);
+  if (!valid_order(order)) return fail(CPATTN_ERR_INVALID_ARG, "unknown ring order");
   if (causal != 0 && causal != 1) return fail(CPATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
   return ok();
 }
 
 // ---- split-KV decode layout
+//
+// n_chunks K/V blocks of at most `cap` rows each.  The decode kernel runs one
+// persistent workgroup per CU that streams its units back to back; about four
+// units per CU of a 256-CU device balance the load without cutting the stream
+// into many short units, so blocks are cut into sub-splits (of at least 256
+// keys) until there are about 1024 units.
 struct DecodeLayout {
   int n_split, split_len, head_blocks, n_part;
   size_t o_bytes, bytes;
 };
 
-DecodeLayout decode_layout(const cpattn_tensor& q, const cpattn_tensor& k, int n_chunks) {
+DecodeLayout decode_layout(const cpattn_tensor& q, int64_t Hkv, int64_t cap, int n_chunks) {
   DecodeLayout L;
-  const int64_t G = q.H / k.H;
+  const int64_t G = q.H / Hkv;
   L.head_blocks = (int)((G + 15) / 16);
-  const int64_t chunk = k.S / n_chunks;
-  const int64_t base_units = q.B * k.H * L.head_blocks * n_chunks;
+  const int64_t base_units = q.B * Hkv * L.head_blocks * n_chunks;
   int ns = 1;
-  // The decode kernel runs one persistent workgroup per CU that streams its
-  // units back to back; about four units per CU of a 256-CU device balance
-  // the load without cutting the stream into many short units.  Splits stay
-  // >= 256 keys.
-  while (base_units * ns < 1024 && chunk / (2 * ns) >= 256 && (int64_t)n_chunks * ns * 2 <= cpattn::kMaxMerge) ns *= 2;
+  while (base_units * ns < 1024 && cap / (2 * ns) >= 256 && (int64_t)n_chunks * ns * 2 <= cpattn::kMaxMerge) ns *= 2;
   L.n_split = ns;
-  const int64_t per = (chunk + ns - 1) / ns;
+  const int64_t per = (cap + ns - 1) / ns;
   L.split_len = (int)((per + 31) / 32 * 32);
   if (L.split_len == 0) L.split_len = 32;
   L.n_part = n_chunks * ns;
@@ -255,13 +304,149 @@ cpattn_status check_workspace(void* ws, size_t have, size_t need) {
   return ok();
 }
 
+// K/V cache shards: n descriptors of one shape, dtype and strides (only the
+// data pointers differ), with the K and V shards alike.
+cpattn_status check_shards(const cpattn_tensor* ks, const cpattn_tensor* vs, int n) {
+  if (ks == nullptr || vs == nullptr) return fail(CPATTN_ERR_INVALID_ARG, "shard arrays are NULL");
+  if (n < 1) return fail(CPATTN_ERR_INVALID_ARG, "the number of shards must be >= 1");
+  if (n > cpattn::kMaxMerge) return fail(CPATTN_ERR_UNSUPPORTED, "more than %d shards", cpattn::kMaxMerge);
+  cpattn_status s;
+  for (int r = 0; r < n; ++r) {
+    if ((s = check_tensor(&ks[r], "k shard", false)) != CPATTN_OK) return s;
+    if ((s = check_tensor(&vs[r], "v shard", false)) != CPATTN_OK) return s;
+    if (ks[r].dtype != ks[0].dtype || vs[r].dtype != ks[0].dtype)
+      return fail(CPATTN_ERR_INVALID_ARG, "shards must share one dtype");
+    if (!same_bshd(ks[r], ks[0]) || !same_strides(ks[r], ks[0]))
+      return fail(CPATTN_ERR_INVALID_ARG, "k shard %d differs in shape or strides from k shard 0", r);
+    if (!same_bshd(vs[r], ks[0]) || !same_strides(vs[r], vs[0]))
+      return fail(CPATTN_ERR_INVALID_ARG, "v shard %d differs in shape or strides", r);
+  }
+  if (ks[0].D != 64 && ks[0].D != 128)
+    return fail(CPATTN_ERR_UNSUPPORTED, "head_dim %lld not supported (64 or 128)", (long long)ks[0].D);
+  return ok();
+}
+
+// Split-KV decode of q against K/V blocks kc[c], vc[c] of len[c] rows (the
+// blocks share strides), then the merge of the partials in block order.
+cpattn_status run_decode(const cpattn_tensor& q, const cpattn_tensor& k, const cpattn_tensor& v, int n_blocks,
+                         const void* const* kc, const void* const* vc, const int64_t* len, const DecodeLayout& L,
+                         cpattn_tensor* out, cpattn_tensor* lse, void* workspace, hipStream_t st) {
+  float* ws_o = static_cast<float*>(workspace);
+  float* ws_l = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.o_bytes);
+  cpattn::DecodeLaunch d;
+  std::memset(&d, 0, sizeof d);
+  d.q = q.data;
+  d.o = ws_o; d.lse = ws_l;
+  d.o_slot = q.B * q.H * q.D; d.o_sb = q.H * q.D; d.o_sh = q.D;
+  d.l_slot = q.B * q.H; d.l_sb = q.H; d.l_sh = 1;
+  d.q_sb = q.stride_b; d.q_sh = q.stride_h;
+  d.k_sb = k.stride_b; d.k_ss = k.stride_s; d.k_sh = k.stride_h;
+  d.v_sb = v.stride_b; d.v_ss = v.stride_s; d.v_sh = v.stride_h;
+  d.B = (int32_t)q.B; d.Hq = (int32_t)q.H; d.Hkv = (int32_t)k.H; d.G = (int32_t)(q.H / k.H);
+  d.n_chunks = n_blocks;
+  d.n_split = L.n_split;
+  d.split_len = L.split_len;
+  d.head_blocks = L.head_blocks;
+  for (int c = 0; c < n_blocks; ++c) {
+    d.kc[c] = kc[c];
+    d.vc[c] = vc[c];
+    d.len[c] = (int32_t)len[c];
+  }
+  hipError_t e = cpattn::launch_decode_bf16(d, (int)q.D, st);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+
+  cpattn::MergeLaunch m;
+  std::memset(&m, 0, sizeof m);
+  m.n = L.n_part;
+  const int64_t part_o = q.B * q.H * q.D, part_l = q.B * q.H;
+  for (int c = 0; c < m.n; ++c) {
+    m.o[c] = ws_o + c * part_o;
+    m.lse[c] = ws_l + c * part_l;
+  }
+  m.out_bf16 = out->dtype == CPATTN_BF16;
+  m.B = (int32_t)q.B; m.S = 1; m.H = (int32_t)q.H; m.D = (int32_t)q.D;
+  m.p_sb = q.H * q.D; m.p_ss = q.H * q.D; m.p_sh = q.D;
+  m.pl_sb = q.H; m.pl_ss = q.H; m.pl_sh = 1;
+  m.out = out->data;
+  m.o_sb = out->stride_b; m.o_ss = out->stride_s; m.o_sh = out->stride_h;
+  if (lse != nullptr) {
+    m.out_lse = static_cast<float*>(lse->data);
+    m.ol_sb = lse->stride_b; m.ol_ss = lse->stride_s; m.ol_sh = lse->stride_h;
+  }
+  e = cpattn::launch_merge(m, st);
+  if (e != hipSuccess) return hip_fail(e, "decode merge launch");
+  return ok();
+}
+
+// Partial attention of the given (q-chunk, kv-chunk) pairs into their
+// workspace slots, in launches of at most kMaxItems pairs.
+cpattn_status launch_ring_items(const cpattn_tensor& q, const cpattn_tensor& k, const cpattn_tensor& v,
+                                const RingLayout& L, bool causal, const std::vector<Pair>& pairs, void* workspace,
+                                void* stream, const char* what) {
+  cpattn::PartialLaunch a = base_partial(q, k, v);
+  a.o = static_cast<float*>(workspace);
+  a.lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.o_bytes);
+  a.o_sh = q.D; a.o_ss = q.H * q.D; a.o_sb = L.Cq * q.H * q.D;
+  a.l_sh = 1; a.l_ss = q.H; a.l_sb = L.Cq * q.H;
+  a.o_slot = L.slot_o;
+  a.l_slot = L.slot_l;
+  a.q_pos0 = L.q0;
+  a.chunk_len = L.Cq;
+  a.kv_chunk_len = L.Ckv;
+  a.Sq = (int32_t)L.Cq;
+  a.Sk = (int32_t)L.Ckv;
+  a.causal = causal ? 1 : 0;
+  size_t i = 0;
+  while (i < pairs.size()) {
+    a.n_items = 0;
+    for (; i < pairs.size() && a.n_items < cpattn::kMaxItems; ++i)
+      a.items[a.n_items++] = cpattn::Item{pairs[i].q, pairs[i].kv, L.slot0[pairs[i].q] + pairs[i].kv, 0};
+    const hipError_t e = launch_partial(a, q.dtype, (int)q.D, (int)L.Cq, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, what);
+  }
+  return ok();
+}
+
+// Keys [0, sk) of the K/V sequence that some query of Q chunk i can see.
+int64_t owner_keys(const RingLayout& L, int i, bool causal) {
+  const int64_t Skv = L.Ckv * L.P;
+  return causal ? std::min<int64_t>(Skv, L.q0 + (i + 1) * L.Cq) : Skv;
+}
+
+cpattn_status ring_merge_impl(const RingLayout& L, int order, const void* workspace, cpattn_tensor* out,
+                              cpattn_tensor* lse, void* stream) {
+  cpattn::RingMergeLaunch m;
+  std::memset(&m, 0, sizeof m);
+  m.ws_o = static_cast<const float*>(workspace);
+  m.ws_l = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + L.o_bytes);
+  m.slot_o = L.slot_o;
+  m.slot_l = L.slot_l;
+  m.P = L.P;
+  m.C = (int32_t)L.Cq; m.B = (int32_t)out->B; m.H = (int32_t)out->H; m.D = (int32_t)out->D;
+  m.pass_q = order == CPATTN_PASS_Q ? 1 : 0;
+  m.out_bf16 = out->dtype == CPATTN_BF16;
+  m.out = out->data;
+  m.o_sb = out->stride_b; m.o_ss = out->stride_s; m.o_sh = out->stride_h;
+  if (lse != nullptr) {
+    m.out_lse = static_cast<float*>(lse->data);
+    m.ol_sb = lse->stride_b; m.ol_ss = lse->stride_s; m.ol_sh = lse->stride_h;
+  }
+  for (int i = 0; i < L.P; ++i) {
+    m.n_vis[i] = L.n_vis[i];
+    m.slot0[i] = L.slot0[i];
+  }
+  const hipError_t e = cpattn::launch_ring_merge(m, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ring merge launch");
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
 
 const char* cpattn_last_error(void) { return g_err.c_str(); }
 
-const char* cpattn_version(void) { return "cpattn 0.1.0 gfx950"; }
+const char* cpattn_version(void) { return "cpattn 0.2.0 gfx950"; }
 
 cpattn_status cpattn_partial(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
                              int64_t q_offset, int64_t kv_offset, int causal, cpattn_tensor* out,
@@ -284,7 +469,8 @@ cpattn_status cpattn_partial(const cpattn_tensor* q, const cpattn_tensor* k, con
     if (causal) visible = std::max<int64_t>(0, std::min<int64_t>(k->S, q_offset - kv_offset + 1));
     cpattn::DecodeLaunch d;
     std::memset(&d, 0, sizeof d);
-    d.q = q->data; d.k = k->data; d.v = v->data;
+    d.q = q->data;
+    d.kc[0] = k->data; d.vc[0] = v->data; d.len[0] = (int32_t)visible;
     d.o = static_cast<float*>(out->data);
     d.lse = static_cast<float*>(lse->data);
     d.o_slot = 0; d.o_sb = out->stride_b; d.o_sh = out->stride_h;
@@ -293,7 +479,6 @@ cpattn_status cpattn_partial(const cpattn_tensor* q, const cpattn_tensor* k, con
     d.k_sb = k->stride_b; d.k_ss = k->stride_s; d.k_sh = k->stride_h;
     d.v_sb = v->stride_b; d.v_ss = v->stride_s; d.v_sh = v->stride_h;
     d.B = (int32_t)q->B; d.Hq = (int32_t)q->H; d.Hkv = (int32_t)k->H; d.G = (int32_t)G;
-    d.Skv = (int32_t)visible;
     d.n_chunks = 1;
     d.n_split = 1;
     d.split_len = (int32_t)((std::max<int64_t>(visible, 1) + 63) / 64 * 64);
@@ -310,12 +495,11 @@ cpattn_status cpattn_partial(const cpattn_tensor* q, const cpattn_tensor* k, con
   a.l_sb = lse->stride_b; a.l_ss = lse->stride_s; a.l_sh = lse->stride_h;
   a.q_pos0 = q_offset;
   a.kv_pos0 = kv_offset;
-  a.chunk_len = 0;
   a.Sq = (int32_t)q->S;
   a.Sk = (int32_t)k->S;
   a.causal = causal;
   a.n_items = 1;
-  a.items[0] = cpattn::Item{0, 0, 0};
+  a.items[0] = cpattn::Item{0, 0, 0, 0};
   const hipError_t e = launch_partial(a, q->dtype, (int)q->D, (int)q->S, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "partial attention launch");
   return ok();
@@ -365,64 +549,67 @@ cpattn_status cpattn_merge(const cpattn_tensor* partials, const cpattn_tensor* l
   return ok();
 }
 
-size_t cpattn_ring_prefill_workspace_size(const cpattn_tensor* q, int n_chunks, cpattn_order order, int causal) {
+size_t cpattn_ring_prefill_workspace_size(const cpattn_tensor* q, const cpattn_tensor* k, int n_chunks, int causal) {
   if (check_tensor(q, "q", false) != CPATTN_OK) return 0;
-  if (n_chunks < 1 || q->S % n_chunks != 0) {
-    fail(CPATTN_ERR_INVALID_ARG, "n_chunks must be >= 1 and divide the sequence length");
+  int64_t Skv = q->S;
+  if (k != nullptr) {
+    if (check_tensor(k, "k", false) != CPATTN_OK) return 0;
+    Skv = k->S;
+  }
+  if (Skv < q->S) {
+    fail(CPATTN_ERR_INVALID_ARG, "k/v must be at least as long as q");
     return 0;
   }
-  if (order != CPATTN_PASS_KV && order != CPATTN_PASS_Q) {
-    fail(CPATTN_ERR_INVALID_ARG, "unknown ring order");
+  if (n_chunks < 1 || n_chunks > cpattn::kMaxMerge || q->S % n_chunks != 0 || Skv % n_chunks != 0) {
+    fail(CPATTN_ERR_INVALID_ARG, "n_chunks must be in [1, %d] and divide both sequence lengths", cpattn::kMaxMerge);
+    return 0;
+  }
+  if (causal != 0 && causal != 1) {
+    fail(CPATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
     return 0;
   }
   ok();
-  return ring_layout(*q, n_chunks, causal != 0).bytes;
+  return ring_layout(*q, Skv, n_chunks, causal != 0).bytes;
 }
 
-// Partial attention of the given (q-chunk, kv-chunk) pairs into their
-// workspace slots, in launches of at most kMaxItems pairs.
-cpattn_status launch_ring_items(const cpattn_tensor& q, const cpattn_tensor& k, const cpattn_tensor& v,
-                                const RingLayout& L, int n_chunks, bool causal, const std::vector<Pair>& pairs,
-                                void* workspace, void* stream, const char* what) {
-  cpattn::PartialLaunch a = base_partial(q, k, v);
-  a.o = static_cast<float*>(workspace);
-  a.lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.o_bytes);
-  a.o_sh = q.D; a.o_ss = q.H * q.D; a.o_sb = L.C * q.H * q.D;
-  a.l_sh = 1; a.l_ss = q.H; a.l_sb = L.C * q.H;
-  a.o_slot = L.slot_o;
-  a.l_slot = L.slot_l;
-  a.chunk_len = L.C;
-  a.Sq = (int32_t)L.C;
-  a.Sk = (int32_t)L.C;
-  a.causal = causal ? 1 : 0;
-  size_t i = 0;
-  while (i < pairs.size()) {
-    a.n_items = 0;
-    for (; i < pairs.size() && a.n_items < cpattn::kMaxItems; ++i)
-      a.items[a.n_items++] = cpattn::Item{pairs[i].q, pairs[i].kv, (int32_t)ring_slot(n_chunks, pairs[i].q, pairs[i].kv, causal)};
-    const hipError_t e = launch_partial(a, q.dtype, (int)q.D, (int)L.C, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, what);
-  }
+cpattn_status cpattn_ring_select_order(const cpattn_tensor* q, const cpattn_tensor* k, int n_chunks, int causal,
+                                       int* order, uint64_t* bytes_pass_kv, uint64_t* bytes_pass_q) {
+  cpattn_status s;
+  if ((s = check_tensor(q, "q", false)) != CPATTN_OK) return s;
+  if ((s = check_tensor(k, "k", false)) != CPATTN_OK) return s;
+  if (order == nullptr) return fail(CPATTN_ERR_INVALID_ARG, "order is NULL");
+  if (q->B != k->B || q->D != k->D || k->H < 1 || q->H % k->H != 0)
+    return fail(CPATTN_ERR_INVALID_ARG, "q and k shapes do not match");
+  if (q->dtype != k->dtype) return fail(CPATTN_ERR_INVALID_ARG, "q and k must share one dtype");
+  if (k->S < q->S) return fail(CPATTN_ERR_INVALID_ARG, "k/v must be at least as long as q");
+  if (n_chunks < 1 || n_chunks > cpattn::kMaxMerge || q->S % n_chunks != 0 || k->S % n_chunks != 0)
+    return fail(CPATTN_ERR_INVALID_ARG, "n_chunks must be in [1, %d] and divide both sequence lengths",
+                cpattn::kMaxMerge);
+  if (causal != 0 && causal != 1) return fail(CPATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
+  const RingLayout L = ring_layout(*q, k->S, n_chunks, causal != 0);
+  const RingBytes rb = ring_bytes(*q, *k, L);
+  *order = rb.pass_q < rb.pass_kv ? CPATTN_PASS_Q : CPATTN_PASS_KV;
+  if (bytes_pass_kv != nullptr) *bytes_pass_kv = rb.pass_kv;
+  if (bytes_pass_q != nullptr) *bytes_pass_q = rb.pass_q;
   return ok();
 }
 
 cpattn_status cpattn_ring_step(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
-                               int n_chunks, cpattn_order order, int causal, int step, void* workspace,
+                               int n_chunks, int order /* cpattn_order */, int causal, int step, void* workspace,
                                size_t workspace_bytes, void* stream) {
   cpattn_status s;
   if ((s = check_ring(q, k, v, n_chunks, order, causal)) != CPATTN_OK) return s;
   if (step < 0 || step >= n_chunks) return fail(CPATTN_ERR_INVALID_ARG, "step %d outside [0, %d)", step, n_chunks);
   if (q->S == 0 || q->B == 0) return ok();
   const bool cz = causal != 0;
-  const RingLayout L = ring_layout(*q, n_chunks, cz);
+  const RingLayout L = ring_layout(*q, k->S, n_chunks, cz);
   if ((s = check_workspace(workspace, workspace_bytes, L.bytes)) != CPATTN_OK) return s;
-
-  return launch_ring_items(*q, *k, *v, L, n_chunks, cz, ring_step(n_chunks, step, order, cz), workspace, stream,
-                           "ring step launch");
+  const int ord = resolve_order(order, *q, *k, L);
+  return launch_ring_items(*q, *k, *v, L, cz, ring_step(L, step, ord), workspace, stream, "ring step launch");
 }
 
 cpattn_status cpattn_ring_step_accumulate(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
-                                          int n_chunks, cpattn_order order, int causal, int step,
+                                          int n_chunks, int order /* cpattn_order */, int causal, int step,
                                           cpattn_tensor* out, cpattn_tensor* lse, void* stream) {
   cpattn_status s;
   if ((s = check_ring(q, k, v, n_chunks, order, causal)) != CPATTN_OK) return s;
@@ -430,119 +617,106 @@ cpattn_status cpattn_ring_step_accumulate(const cpattn_tensor* q, const cpattn_t
   if ((s = check_out(out, lse, *q, false, true)) != CPATTN_OK) return s;
   if (q->S == 0 || q->B == 0) return ok();
   const bool cz = causal != 0;
-  const int64_t C = q->S / n_chunks;
+  const RingLayout L = ring_layout(*q, k->S, n_chunks, cz);
+  const int ord = resolve_order(order, *q, *k, L);
   cpattn::PartialLaunch a = base_partial(*q, *k, *v);
   a.o = static_cast<float*>(out->data);
   a.o_sb = out->stride_b; a.o_ss = out->stride_s; a.o_sh = out->stride_h;
-  a.o_slot = C * out->stride_s;  // owner i's rows start at row iC
+  a.o_slot = L.Cq * out->stride_s;  // owner i's rows start at row i Cq
   a.lse = static_cast<float*>(lse->data);
   a.l_sb = lse->stride_b; a.l_ss = lse->stride_s; a.l_sh = lse->stride_h;
-  a.l_slot = C * lse->stride_s;
-  a.chunk_len = C;
-  a.Sq = (int32_t)C;
-  a.Sk = (int32_t)C;
+  a.l_slot = L.Cq * lse->stride_s;
+  a.q_pos0 = L.q0;
+  a.chunk_len = L.Cq;
+  a.kv_chunk_len = L.Ckv;
+  a.Sq = (int32_t)L.Cq;
+  a.Sk = (int32_t)L.Ckv;
   a.causal = cz ? 1 : 0;
   // step 0 is every owner's first arrival (its own chunk): it writes; later steps merge
   a.accumulate = step > 0 ? 1 : 0;
   a.n_items = 0;
-  for (const Pair& p : ring_step(n_chunks, step, order, cz)) a.items[a.n_items++] = cpattn::Item{p.q, p.kv, p.q, 0};
+  for (const Pair& p : ring_step(L, step, ord)) a.items[a.n_items++] = cpattn::Item{p.q, p.kv, p.q, 0};
   if (a.n_items == 0) return ok();
-  const hipError_t e = launch_partial(a, q->dtype, (int)q->D, (int)C, static_cast<hipStream_t>(stream));
+  const hipError_t e = launch_partial(a, q->dtype, (int)q->D, (int)L.Cq, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "accumulating ring step launch");
   return ok();
 }
 
-cpattn_status cpattn_ring_merge(int n_chunks, cpattn_order order, int causal, const void* workspace,
+cpattn_status cpattn_ring_merge(int n_chunks, int order /* cpattn_order */, int causal, int64_t kv_len, const void* workspace,
                                 size_t workspace_bytes, cpattn_tensor* out, cpattn_tensor* lse, void* stream) {
   cpattn_status s;
   if (n_chunks < 1) return fail(CPATTN_ERR_INVALID_ARG, "n_chunks must be >= 1");
   if (n_chunks > cpattn::kMaxMerge)
     return fail(CPATTN_ERR_UNSUPPORTED, "n_chunks above %d not supported", cpattn::kMaxMerge);
-  if (order != CPATTN_PASS_KV && order != CPATTN_PASS_Q) return fail(CPATTN_ERR_INVALID_ARG, "unknown ring order");
+  if (order != CPATTN_PASS_KV && order != CPATTN_PASS_Q)
+    return fail(CPATTN_ERR_INVALID_ARG, "ring merge needs the order the steps ran in (Pass-KV or Pass-Q)");
   if (causal != 0 && causal != 1) return fail(CPATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
   if ((s = check_tensor(out, "out", false)) != CPATTN_OK) return s;
   if (out->D != 64 && out->D != 128)
     return fail(CPATTN_ERR_UNSUPPORTED, "head_dim %lld not supported (64 or 128)", (long long)out->D);
   if ((s = check_out(out, lse, *out, true, false)) != CPATTN_OK) return s;
-  if (out->S % n_chunks != 0)
-    return fail(CPATTN_ERR_INVALID_ARG, "sequence length %lld not divisible by n_chunks %d", (long long)out->S, n_chunks);
+  if (kv_len < out->S) return fail(CPATTN_ERR_INVALID_ARG, "kv_len %lld shorter than the output's %lld rows",
+                                   (long long)kv_len, (long long)out->S);
+  if (out->S % n_chunks != 0 || kv_len % n_chunks != 0)
+    return fail(CPATTN_ERR_INVALID_ARG, "sequence lengths %lld (q) and %lld (k/v) must both be divisible by n_chunks %d",
+                (long long)out->S, (long long)kv_len, n_chunks);
   if (out->S == 0 || out->B == 0) return ok();
-  const bool cz = causal != 0;
-  const RingLayout L = ring_layout(*out, n_chunks, cz);
+  const RingLayout L = ring_layout(*out, kv_len, n_chunks, causal != 0);
   if ((s = check_workspace(const_cast<void*>(workspace), workspace_bytes, L.bytes)) != CPATTN_OK) return s;
-
-  cpattn::RingMergeLaunch m;
-  std::memset(&m, 0, sizeof m);
-  m.ws_o = static_cast<const float*>(workspace);
-  m.ws_l = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + L.o_bytes);
-  m.slot_o = L.slot_o;
-  m.slot_l = L.slot_l;
-  m.P = n_chunks;
-  m.C = (int32_t)L.C; m.B = (int32_t)out->B; m.H = (int32_t)out->H; m.D = (int32_t)out->D;
-  m.causal = cz ? 1 : 0;
-  m.pass_q = order == CPATTN_PASS_Q ? 1 : 0;
-  m.out_bf16 = out->dtype == CPATTN_BF16;
-  m.out = out->data;
-  m.o_sb = out->stride_b; m.o_ss = out->stride_s; m.o_sh = out->stride_h;
-  if (lse != nullptr) {
-    m.out_lse = static_cast<float*>(lse->data);
-    m.ol_sb = lse->stride_b; m.ol_ss = lse->stride_s; m.ol_sh = lse->stride_h;
-  }
-  const hipError_t e = cpattn::launch_ring_merge(m, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "ring merge launch");
-  return ok();
+  return ring_merge_impl(L, order, workspace, out, lse, stream);
 }
 
 cpattn_status cpattn_ring_prefill(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
-                                  int n_chunks, cpattn_order order, int causal, cpattn_tensor* out,
+                                  int n_chunks, int order /* cpattn_order */, int causal, cpattn_tensor* out,
                                   cpattn_tensor* lse, void* workspace, size_t workspace_bytes, void* stream) {
   cpattn_status s;
   if ((s = check_ring(q, k, v, n_chunks, order, causal)) != CPATTN_OK) return s;
   if ((s = check_out(out, lse, *q, true, false)) != CPATTN_OK) return s;
   if (q->S == 0 || q->B == 0) return ok();
-  if ((s = check_workspace(workspace, workspace_bytes, ring_layout(*q, n_chunks, causal != 0).bytes)) != CPATTN_OK)
-    return s;
+  const bool cz = causal != 0;
+  const RingLayout L = ring_layout(*q, k->S, n_chunks, cz);
+  if ((s = check_workspace(workspace, workspace_bytes, L.bytes)) != CPATTN_OK) return s;
+  const int ord = resolve_order(order, *q, *k, L);
   // On one device the pairs of all ring steps are independent, so they go
   // out together; each lands in its own slot, and the merge reads the slots
-  // in the ring order's arrival order.  The workgroups of a launch are dealt
-  // to the XCDs in contiguous eighths of the grid, so the diagonal pairs
-  // (half the work of a full pair under the causal mask) are spread evenly
-  // through the list: every eighth gets its share of them.
-  const bool cz = causal != 0;
-  const int64_t C = q->S / n_chunks;
-  if (q->dtype == CPATTN_BF16 && q->D == 128 && C % 64 == 0 && C <= 4096) {
-    // Chunks of up to 4096 tokens: one work item per owner whose query chunk
-    // walks every key it sees in one pass (as in the fused prefill), writing
-    // each kv chunk's partial to that pair's slot at the chunk boundary and
-    // restarting the softmax there exactly as a launch of the pair alone
-    // would -- the same partials, bit for bit, without a workgroup prologue
-    // per pair (+9% with 1024-token chunks; with 8192-token chunks the
-    // boundary flushes cost more than the prologues they save, -1%).
-    const RingLayout L = ring_layout(*q, n_chunks, cz);
+  // in the ring order's arrival order.
+  if (q->dtype == CPATTN_BF16 && q->D == 128 && L.Ckv % 64 == 0 && L.Ckv <= 4096) {
+    // K/V chunks of up to 4096 tokens: one work item per owner whose query
+    // chunk walks every key it sees in one pass (as in the fused prefill),
+    // writing each kv chunk's partial to that pair's slot at the chunk
+    // boundary and restarting the softmax there exactly as a launch of the
+    // pair alone would -- the same partials, bit for bit, without a workgroup
+    // prologue per pair (+9% with 1024-token chunks; with 8192-token chunks
+    // the boundary flushes cost more than the prologues they save, -1%).
     cpattn::PartialLaunch a = base_partial(*q, *k, *v);
     a.o = static_cast<float*>(workspace);
     a.lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.o_bytes);
-    a.o_sh = q->D; a.o_ss = q->H * q->D; a.o_sb = L.C * q->H * q->D;
-    a.l_sh = 1; a.l_ss = q->H; a.l_sb = L.C * q->H;
+    a.o_sh = q->D; a.o_ss = q->H * q->D; a.o_sb = L.Cq * q->H * q->D;
+    a.l_sh = 1; a.l_ss = q->H; a.l_sb = L.Cq * q->H;
     a.o_slot = L.slot_o;
     a.l_slot = L.slot_l;
-    a.chunk_len = C;
-    a.Sq = (int32_t)C;
-    a.Sk = (int32_t)q->S;
+    a.q_pos0 = L.q0;
+    a.chunk_len = L.Cq;
+    a.kv_chunk_len = L.Ckv;
+    a.Sq = (int32_t)L.Cq;
+    a.Sk = (int32_t)k->S;
     a.causal = cz ? 1 : 0;
-    a.seg_tiles = (int32_t)(C / 64);
+    a.seg_tiles = (int32_t)(L.Ckv / 64);
     a.xcd_order = 0;  // launch order, heaviest owner first
     a.n_items = 0;
     for (int i = n_chunks - 1; i >= 0; --i)
-      a.items[a.n_items++] = cpattn::Item{i, 0, (int32_t)ring_slot(n_chunks, i, 0, cz),
-                                          (int32_t)(cz ? (i + 1) * C : q->S)};
-    const hipError_t e = launch_partial(a, q->dtype, (int)q->D, (int)C, static_cast<hipStream_t>(stream));
+      a.items[a.n_items++] = cpattn::Item{i, 0, L.slot0[i], (int32_t)owner_keys(L, i, cz)};
+    const hipError_t e = launch_partial(a, q->dtype, (int)q->D, (int)L.Cq, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "ring prefill launch");
-    return cpattn_ring_merge(n_chunks, order, causal, workspace, workspace_bytes, out, lse, stream);
+    return ring_merge_impl(L, ord, workspace, out, lse, stream);
   }
+  // The workgroups of a launch are dealt to the XCDs in contiguous eighths of
+  // the grid, so the diagonal pairs (half the work of a full pair under the
+  // causal mask at equal lengths) are spread evenly through the list: every
+  // eighth gets its share of them.
   std::vector<Pair> full, diag;
   for (int step = 0; step < n_chunks; ++step)
-    for (const Pair& p : ring_step(n_chunks, step, order, cz)) (cz && p.q == p.kv ? diag : full).push_back(p);
+    for (const Pair& p : ring_step(L, step, ord)) (cz && p.q == p.kv ? diag : full).push_back(p);
   std::vector<Pair> pairs;
   pairs.reserve(full.size() + diag.size());
   const size_t n = full.size() + diag.size();
@@ -552,10 +726,9 @@ cpattn_status cpattn_ring_prefill(const cpattn_tensor* q, const cpattn_tensor* k
     const bool take_diag = di < diag.size() && (fi == full.size() || (2 * di + 1) * n <= 2 * i * diag.size() + diag.size());
     pairs.push_back(take_diag ? diag[di++] : full[fi++]);
   }
-  if ((s = launch_ring_items(*q, *k, *v, ring_layout(*q, n_chunks, cz), n_chunks, cz, pairs, workspace, stream,
-                             "ring prefill launch")) != CPATTN_OK)
+  if ((s = launch_ring_items(*q, *k, *v, L, cz, pairs, workspace, stream, "ring prefill launch")) != CPATTN_OK)
     return s;
-  return cpattn_ring_merge(n_chunks, order, causal, workspace, workspace_bytes, out, lse, stream);
+  return ring_merge_impl(L, ord, workspace, out, lse, stream);
 }
 
 cpattn_status cpattn_ring_prefill_fused(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
@@ -566,29 +739,31 @@ cpattn_status cpattn_ring_prefill_fused(const cpattn_tensor* q, const cpattn_ten
   if ((s = check_out(out, lse, *q, false, false)) != CPATTN_OK) return s;
   if (q->S == 0 || q->B == 0) return ok();
   const int P = n_chunks;
-  const int64_t C = q->S / P;
+  const bool cz = causal != 0;
+  const RingLayout L = ring_layout(*q, k->S, P, cz);
   cpattn::PartialLaunch a = base_partial(*q, *k, *v);
   a.o = static_cast<float*>(out->data);
   a.o_sb = out->stride_b; a.o_ss = out->stride_s; a.o_sh = out->stride_h;
-  a.o_slot = C * out->stride_s;  // owner i's rows start at row iC of the output
+  a.o_slot = L.Cq * out->stride_s;  // owner i's rows start at row i Cq of the output
   if (lse != nullptr) {
     a.lse = static_cast<float*>(lse->data);
     a.l_sb = lse->stride_b; a.l_ss = lse->stride_s; a.l_sh = lse->stride_h;
-    a.l_slot = C * lse->stride_s;
+    a.l_slot = L.Cq * lse->stride_s;
   }
-  a.chunk_len = C;
-  a.Sq = (int32_t)C;
-  a.Sk = (int32_t)q->S;
+  a.q_pos0 = L.q0;
+  a.chunk_len = L.Cq;
+  a.kv_chunk_len = L.Ckv;
+  a.Sq = (int32_t)L.Cq;
+  a.Sk = (int32_t)k->S;
   a.causal = causal;
-  // One item per owner: Q chunk i against the keys it sees ([0, (i+1)C) under
-  // the causal mask, all of them otherwise), accumulated in one pass.  The
-  // owners' costs differ up to P-fold, so the grid keeps its launch order
-  // (consecutive workgroups go to different XCDs) with the heaviest owner first.
+  // One item per owner: Q chunk i against the keys it sees, accumulated in
+  // one pass.  The owners' costs differ up to P-fold, so the grid keeps its
+  // launch order (consecutive workgroups go to different XCDs) with the
+  // heaviest owner first.
   a.xcd_order = 0;
   a.n_items = 0;
-  for (int i = P - 1; i >= 0; --i)
-    a.items[a.n_items++] = cpattn::Item{i, 0, i, (int32_t)(causal ? (i + 1) * C : q->S)};
-  const hipError_t e = launch_partial(a, q->dtype, (int)q->D, (int)C, static_cast<hipStream_t>(stream));
+  for (int i = P - 1; i >= 0; --i) a.items[a.n_items++] = cpattn::Item{i, 0, i, (int32_t)owner_keys(L, i, cz)};
+  const hipError_t e = launch_partial(a, q->dtype, (int)q->D, (int)L.Cq, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "fused ring prefill launch");
   return ok();
 }
@@ -604,7 +779,7 @@ size_t cpattn_splitkv_decode_workspace_size(const cpattn_tensor* q, const cpattn
     return 0;
   }
   ok();
-  return decode_layout(*q, *k, n_chunks).bytes;
+  return decode_layout(*q, k->H, k->S / n_chunks, n_chunks).bytes;
 }
 
 cpattn_status cpattn_splitkv_decode(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
@@ -614,52 +789,128 @@ cpattn_status cpattn_splitkv_decode(const cpattn_tensor* q, const cpattn_tensor*
   if ((s = check_decode(q, k, v, n_chunks)) != CPATTN_OK) return s;
   if ((s = check_out(out, lse, *q, true, false)) != CPATTN_OK) return s;
   if (q->B == 0) return ok();
-  const DecodeLayout L = decode_layout(*q, *k, n_chunks);
+  const int64_t C = k->S / n_chunks;
+  const DecodeLayout L = decode_layout(*q, k->H, C, n_chunks);
   if ((s = check_workspace(workspace, workspace_bytes, L.bytes)) != CPATTN_OK) return s;
-
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  float* ws_o = static_cast<float*>(workspace);
-  float* ws_l = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.o_bytes);
-
-  cpattn::DecodeLaunch d;
-  std::memset(&d, 0, sizeof d);
-  d.q = q->data; d.k = k->data; d.v = v->data;
-  d.o = ws_o; d.lse = ws_l;
-  d.o_slot = q->B * q->H * q->D; d.o_sb = q->H * q->D; d.o_sh = q->D;
-  d.l_slot = q->B * q->H; d.l_sb = q->H; d.l_sh = 1;
-  d.q_sb = q->stride_b; d.q_sh = q->stride_h;
-  d.k_sb = k->stride_b; d.k_ss = k->stride_s; d.k_sh = k->stride_h;
-  d.v_sb = v->stride_b; d.v_ss = v->stride_s; d.v_sh = v->stride_h;
-  d.B = (int32_t)q->B; d.Hq = (int32_t)q->H; d.Hkv = (int32_t)k->H; d.G = (int32_t)(q->H / k->H);
-  d.Skv = (int32_t)k->S;
-  d.n_chunks = n_chunks;
-  d.n_split = L.n_split;
-  d.split_len = L.split_len;
-  d.head_blocks = L.head_blocks;
-  hipError_t e = cpattn::launch_decode_bf16(d, (int)q->D, st);
-  if (e != hipSuccess) return hip_fail(e, "decode launch");
-
-  cpattn::MergeLaunch m;
-  std::memset(&m, 0, sizeof m);
-  m.n = L.n_part;
-  const int64_t part_o = q->B * q->H * q->D, part_l = q->B * q->H;
-  for (int c = 0; c < m.n; ++c) {
-    m.o[c] = ws_o + c * part_o;
-    m.lse[c] = ws_l + c * part_l;
+  const void* kc[cpattn::kMaxMerge];
+  const void* vc[cpattn::kMaxMerge];
+  int64_t len[cpattn::kMaxMerge];
+  for (int c = 0; c < n_chunks; ++c) {
+    kc[c] = static_cast<const __bf16*>(k->data) + c * C * k->stride_s;
+    vc[c] = static_cast<const __bf16*>(v->data) + c * C * v->stride_s;
+    len[c] = C;
   }
-  m.out_bf16 = out->dtype == CPATTN_BF16;
-  m.B = (int32_t)q->B; m.S = 1; m.H = (int32_t)q->H; m.D = (int32_t)q->D;
-  m.p_sb = q->H * q->D; m.p_ss = q->H * q->D; m.p_sh = q->D;
-  m.pl_sb = q->H; m.pl_ss = q->H; m.pl_sh = 1;
-  m.out = out->data;
-  m.o_sb = out->stride_b; m.o_ss = out->stride_s; m.o_sh = out->stride_h;
-  if (lse != nullptr) {
-    m.out_lse = static_cast<float*>(lse->data);
-    m.ol_sb = lse->stride_b; m.ol_ss = lse->stride_s; m.ol_sh = lse->stride_h;
+  return run_decode(*q, *k, *v, n_chunks, kc, vc, len, L, out, lse, workspace, static_cast<hipStream_t>(stream));
+}
+
+cpattn_status cpattn_kv_cache_write(const cpattn_tensor* k, const cpattn_tensor* v, int n_chunks,
+                                    const cpattn_tensor* k_shards, const cpattn_tensor* v_shards, void* stream) {
+  cpattn_status s;
+  if ((s = check_tensor(k, "k", false)) != CPATTN_OK) return s;
+  if ((s = check_tensor(v, "v", false)) != CPATTN_OK) return s;
+  if (!same_bshd(*k, *v) || k->dtype != v->dtype) return fail(CPATTN_ERR_INVALID_ARG, "k and v differ in shape or dtype");
+  if ((s = check_shards(k_shards, v_shards, n_chunks)) != CPATTN_OK) return s;
+  if (k->S % n_chunks != 0)
+    return fail(CPATTN_ERR_INVALID_ARG, "sequence length %lld not divisible by n_chunks %d", (long long)k->S, n_chunks);
+  const cpattn_tensor& sh = k_shards[0];
+  if (sh.dtype != k->dtype || sh.B != k->B || sh.H != k->H || sh.D != k->D)
+    return fail(CPATTN_ERR_INVALID_ARG, "shards must match k/v in dtype, batch, heads and head_dim");
+  const int64_t C = k->S / n_chunks;
+  if (sh.S < C) return fail(CPATTN_ERR_INVALID_ARG, "shards hold %lld rows, a chunk has %lld", (long long)sh.S, (long long)C);
+  if (C == 0 || k->B == 0 || k->H == 0) return ok();
+  const int64_t eb = elem_bytes(k->dtype);
+  for (int t = 0; t < 2; ++t) {
+    const cpattn_tensor& src = t == 0 ? *k : *v;
+    const cpattn_tensor* dst = t == 0 ? k_shards : v_shards;
+    cpattn::CopyLaunch c;
+    std::memset(&c, 0, sizeof c);
+    c.n_jobs = n_chunks;
+    c.elem_bytes = (int32_t)eb;
+    c.B = (int32_t)src.B; c.rows = (int32_t)C; c.H = (int32_t)src.H; c.D = (int32_t)src.D;
+    c.s_sb = src.stride_b; c.s_ss = src.stride_s; c.s_sh = src.stride_h;
+    c.d_sb = dst[0].stride_b; c.d_ss = dst[0].stride_s; c.d_sh = dst[0].stride_h;
+    for (int r = 0; r < n_chunks; ++r) {
+      c.src[r] = static_cast<const char*>(src.data) + r * C * src.stride_s * eb;
+      c.dst[r] = dst[r].data;
+    }
+    const hipError_t e = cpattn::launch_copy(c, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "cache write launch");
   }
-  e = cpattn::launch_merge(m, st);
-  if (e != hipSuccess) return hip_fail(e, "decode merge launch");
   return ok();
+}
+
+cpattn_status cpattn_kv_cache_append(const cpattn_tensor* k_new, const cpattn_tensor* v_new,
+                                     const cpattn_tensor* k_shard, const cpattn_tensor* v_shard, int64_t row,
+                                     void* stream) {
+  cpattn_status s;
+  if ((s = check_tensor(k_new, "k_new", false)) != CPATTN_OK) return s;
+  if ((s = check_tensor(v_new, "v_new", false)) != CPATTN_OK) return s;
+  if (!same_bshd(*k_new, *v_new) || k_new->dtype != v_new->dtype)
+    return fail(CPATTN_ERR_INVALID_ARG, "k_new and v_new differ in shape or dtype");
+  if ((s = check_shards(k_shard, v_shard, 1)) != CPATTN_OK) return s;
+  if (k_shard->dtype != k_new->dtype || k_shard->B != k_new->B || k_shard->H != k_new->H || k_shard->D != k_new->D)
+    return fail(CPATTN_ERR_INVALID_ARG, "the shard must match the new rows in dtype, batch, heads and head_dim");
+  if (row < 0 || row + k_new->S > k_shard->S)
+    return fail(CPATTN_ERR_INVALID_ARG, "rows [%lld, %lld) do not fit a shard of %lld rows", (long long)row,
+                (long long)(row + k_new->S), (long long)k_shard->S);
+  if (k_new->S == 0 || k_new->B == 0 || k_new->H == 0) return ok();
+  const int64_t eb = elem_bytes(k_new->dtype);
+  for (int t = 0; t < 2; ++t) {
+    const cpattn_tensor& src = t == 0 ? *k_new : *v_new;
+    const cpattn_tensor& dst = t == 0 ? *k_shard : *v_shard;
+    cpattn::CopyLaunch c;
+    std::memset(&c, 0, sizeof c);
+    c.n_jobs = 1;
+    c.elem_bytes = (int32_t)eb;
+    c.B = (int32_t)src.B; c.rows = (int32_t)src.S; c.H = (int32_t)src.H; c.D = (int32_t)src.D;
+    c.s_sb = src.stride_b; c.s_ss = src.stride_s; c.s_sh = src.stride_h;
+    c.d_sb = dst.stride_b; c.d_ss = dst.stride_s; c.d_sh = dst.stride_h;
+    c.src[0] = src.data;
+    c.dst[0] = static_cast<char*>(dst.data) + row * dst.stride_s * eb;
+    const hipError_t e = cpattn::launch_copy(c, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "cache append launch");
+  }
+  return ok();
+}
+
+size_t cpattn_cp_decode_workspace_size(const cpattn_tensor* q, const cpattn_tensor* k_shards, int n_shards) {
+  if (check_tensor(q, "q", false) != CPATTN_OK) return 0;
+  if (k_shards == nullptr || n_shards < 1 || n_shards > cpattn::kMaxMerge) {
+    fail(CPATTN_ERR_INVALID_ARG, "need 1 to %d shard descriptors", cpattn::kMaxMerge);
+    return 0;
+  }
+  if (check_tensor(&k_shards[0], "k shard", false) != CPATTN_OK) return 0;
+  if (k_shards[0].H < 1 || q->H % k_shards[0].H != 0) {
+    fail(CPATTN_ERR_INVALID_ARG, "Hq must be a positive multiple of Hkv");
+    return 0;
+  }
+  ok();
+  return decode_layout(*q, k_shards[0].H, k_shards[0].S, n_shards).bytes;
+}
+
+cpattn_status cpattn_cp_decode(const cpattn_tensor* q, const cpattn_tensor* k_shards, const cpattn_tensor* v_shards,
+                               const int64_t* shard_len, int n_shards, cpattn_tensor* out, cpattn_tensor* lse,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  cpattn_status s;
+  if ((s = check_shards(k_shards, v_shards, n_shards)) != CPATTN_OK) return s;
+  if ((s = check_decode(q, &k_shards[0], &v_shards[0], 1)) != CPATTN_OK) return s;
+  if (shard_len == nullptr) return fail(CPATTN_ERR_INVALID_ARG, "shard_len is NULL");
+  for (int r = 0; r < n_shards; ++r)
+    if (shard_len[r] < 0 || shard_len[r] > k_shards[0].S)
+      return fail(CPATTN_ERR_INVALID_ARG, "shard %d: length %lld outside [0, %lld]", r, (long long)shard_len[r],
+                  (long long)k_shards[0].S);
+  if ((s = check_out(out, lse, *q, true, false)) != CPATTN_OK) return s;
+  if (q->B == 0) return ok();
+  const DecodeLayout L = decode_layout(*q, k_shards[0].H, k_shards[0].S, n_shards);
+  if ((s = check_workspace(workspace, workspace_bytes, L.bytes)) != CPATTN_OK) return s;
+  const void* kc[cpattn::kMaxMerge];
+  const void* vc[cpattn::kMaxMerge];
+  for (int r = 0; r < n_shards; ++r) {
+    kc[r] = k_shards[r].data;
+    vc[r] = v_shards[r].data;
+  }
+  return run_decode(*q, k_shards[0], v_shards[0], n_shards, kc, vc, shard_len, L, out, lse, workspace,
+                    static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

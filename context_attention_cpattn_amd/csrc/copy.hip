@@ -1,0 +1,51 @@
+// Row copies into KV-cache shards.
+//
+// The prefill constructs the KV cache of every layer and decode reads (and
+// extends) it ("Scaling LLM Inference", techreport.ngo rewrite, "Why
+// Parallelism Defines LLM Serving Cost"); with the sequence cut across CP
+// ranks, each rank's shard of the cache holds its own chunk's K/V.  These
+// copies put a prefill's chunks into their shards and append new tokens.
+//
+// Bandwidth bound: one thread per 16-byte piece, consecutive threads on
+// consecutive pieces of a [H, D] token row, so both sides are read and
+// written in whole cache lines when the rows are contiguous.
+#include "device.h"
+#include "internal.h"
+
+namespace cpattn {
+namespace {
+
+__global__ __launch_bounds__(256) void copy_rows_kernel(const CopyLaunch a, const int64_t pieces_per_job) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = pieces_per_job * a.n_jobs;
+  if (t >= total) return;
+  const int job = (int)(t / pieces_per_job);
+  int64_t r = t - job * pieces_per_job;
+  const int ppr = a.D * a.elem_bytes / 16;  // pieces per (token, head) row
+  const int pc = (int)(r % ppr);
+  r /= ppr;
+  const int h = (int)(r % a.H);
+  r /= a.H;
+  const int64_t s = r % a.rows;
+  const int64_t b = r / a.rows;
+  const int64_t e_per_piece = 16 / a.elem_bytes;
+  const int64_t so = b * a.s_sb + s * a.s_ss + h * a.s_sh + pc * e_per_piece;
+  const int64_t dof = b * a.d_sb + s * a.d_ss + h * a.d_sh + pc * e_per_piece;
+  const uint8_t* src = static_cast<const uint8_t*>(a.src[job]) + so * a.elem_bytes;
+  uint8_t* dst = static_cast<uint8_t*>(a.dst[job]) + dof * a.elem_bytes;
+  *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+}
+
+}  // namespace
+
+hipError_t launch_copy(const CopyLaunch& a, hipStream_t s) {
+  const long long per_job = (long long)a.B * a.rows * a.H * (a.D * a.elem_bytes / 16);
+  const long long total = per_job * a.n_jobs;
+  if (total <= 0) return hipSuccess;
+  const long long blocks = (total + 255) / 256;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(copy_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a, (int64_t)per_job);
+  return hipGetLastError();
+}
+
+}  // namespace cpattn

@@ -7,7 +7,10 @@
 // HBM, so the kernel is organised to keep enough bytes in flight per CU.  A
 // work unit is (batch, KV head, block of up to 16 query heads sharing it,
 // chunk, sub-split); each unit writes a partial (O normalised, LSE) to the
-// workspace, and the partials are merged afterwards.
+// workspace, and the partials are merged afterwards.  Every chunk has a base
+// pointer and a length of its own, so the chunks may be the equal pieces of
+// one cache or the shards of a cache cut across CP ranks; a unit that finds no
+// key in its range writes the empty partial (O = 0, LSE = -inf).
 //
 // The 16 query heads of a KV head form the 16 columns of a 16x16x32 bf16
 // MFMA: S^T = K Q^T puts keys on rows, so a lane holds 4 keys of one head and
@@ -87,7 +90,6 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeLaunch a
   const int x = lane & 15;   // head within the block (MFMA column) / row within a 16-row block
   const int g4 = lane >> 4;  // lane group
   const int s16 = x;
-  const int chunk_len = a.Skv / a.n_chunks;
 
   struct Unit {
     int b, kvh, hb, c, sp, k_lo, nt, lim_last, rot;
@@ -100,8 +102,8 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeLaunch a
     r.hb = u % a.head_blocks; u /= a.head_blocks;
     r.kvh = u % a.Hkv;
     r.b = u / a.Hkv;
-    r.k_lo = r.c * chunk_len + r.sp * a.split_len;
-    const int k_hi = min(r.k_lo + a.split_len, (r.c + 1) * chunk_len);
+    r.k_lo = r.sp * a.split_len;  // rows of block c
+    const int k_hi = min(r.k_lo + a.split_len, a.len[r.c]);
     const int n = max(0, k_hi - r.k_lo);
     r.nt = (n + TK - 1) / TK;
     r.lim_last = n - (r.nt - 1) * TK;  // keys in the last tile
@@ -135,8 +137,8 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(const DecodeLaunch a
     if (tt >= fU.nt) tt -= fU.nt;
     const int n_keys = (tt == fU.nt - 1) ? fU.lim_last : TK;
     const int k0 = fU.k_lo + tt * TK;
-    const __bf16* kb = static_cast<const __bf16*>(a.k) + fU.b * a.k_sb + fU.kvh * a.k_sh;
-    const __bf16* vb = static_cast<const __bf16*>(a.v) + fU.b * a.v_sb + fU.kvh * a.v_sh;
+    const __bf16* kb = static_cast<const __bf16*>(a.kc[fU.c]) + fU.b * a.k_sb + fU.kvh * a.k_sh;
+    const __bf16* vb = static_cast<const __bf16*>(a.vc[fU.c]) + fU.b * a.v_sb + fU.kvh * a.v_sh;
     const uint32_t dst = lbase + stage * STAGE;
 #pragma unroll
     for (int i = 0; i < KP; ++i) {

@@ -13,7 +13,7 @@ static_assert(kMaxMerge <= kMaxItems, "the pairs of one ring step (at most kMaxM
 
 // One (Q block, K/V block) pair of a launch.  Pointers are derived from the
 // launch's base pointers: Q rows start at q_chunk * chunk_len, K/V rows at
-// kv_chunk * chunk_len, and the outputs go to slot `slot` of the output base.
+// kv_chunk * kv_chunk_len, and the outputs go to slot `slot` of the output base.
 struct Item {
   int32_t q_chunk;
   int32_t kv_chunk;
@@ -34,7 +34,8 @@ struct PartialLaunch {
   int64_t l_sb, l_ss, l_sh;
   int64_t o_slot, l_slot;    // element distance between output slots
   int64_t q_pos0, kv_pos0;   // global position of row 0 of chunk 0
-  int64_t chunk_len;         // rows per chunk (used only to derive item pointers)
+  int64_t chunk_len;         // Q rows per chunk (used only to derive item pointers)
+  int64_t kv_chunk_len;      // K/V rows per chunk
   int32_t B, Sq, Sk, Hq, G;  // Sq/Sk: rows of one Q/K/V block; G = Hq / Hkv
   int32_t causal;
   int32_t n_items;
@@ -61,24 +62,28 @@ struct MergeLaunch {
 
 // Merge of a ring's workspace slots into the final output: every owner i
 // merges its partials in the ring order's arrival order (computed in the
-// kernel), all owners in one launch.
+// kernel), all owners in one launch.  Owner i sees K/V chunks [0, n_vis[i])
+// and its pair with K/V chunk j sits in slot slot0[i] + j.
 struct RingMergeLaunch {
   const float* ws_o;          // slot t: O [B][C][H][D] at ws_o + t * slot_o
   const float* ws_l;          // slot t: LSE [B][C][H] at ws_l + t * slot_l
   int64_t slot_o, slot_l;
-  int32_t P, C, B, H, D;
-  int32_t causal, pass_q;     // ring order: 0 = Pass-KV, 1 = Pass-Q
+  int32_t P, C, B, H, D;      // C: query rows per chunk
+  int32_t pass_q;             // ring order: 0 = Pass-KV, 1 = Pass-Q
   int32_t out_bf16;
   void* out;                  // [B][P*C][H][D]
   int64_t o_sb, o_ss, o_sh;
   float* out_lse;             // may be null
   int64_t ol_sb, ol_ss, ol_sh;
+  int32_t n_vis[kMaxMerge];
+  int32_t slot0[kMaxMerge];
 };
 
+// Split-KV decode over n_chunks K/V blocks, each at its own base pointer (the
+// chunks of one cache, or the shards of a cache cut across CP ranks); every
+// block shares the element strides below.
 struct DecodeLaunch {
   const void* q;  // bf16 [B, 1, Hq, D]
-  const void* k;  // bf16 [B, Skv, Hkv, D]
-  const void* v;
   float* o;       // partial p, batch b, head h at o + p*o_slot + b*o_sb + h*o_sh (D contiguous)
   float* lse;     // partial LSE at lse + p*l_slot + b*l_sb + h*l_sh
   int64_t o_slot, o_sb, o_sh;
@@ -86,10 +91,25 @@ struct DecodeLaunch {
   int64_t q_sb, q_sh;
   int64_t k_sb, k_ss, k_sh;
   int64_t v_sb, v_ss, v_sh;
-  int32_t B, Hq, Hkv, G, Skv;
+  int32_t B, Hq, Hkv, G;
   int32_t n_chunks, n_split;  // partial p = chunk * n_split + split
   int32_t split_len;          // keys per split (multiple of 32, last split may be shorter)
   int32_t head_blocks;        // ceil(G / 16)
+  const void* kc[kMaxMerge];  // bf16 block c: [B, len[c], Hkv, D] at kc[c] / vc[c]
+  const void* vc[kMaxMerge];
+  int32_t len[kMaxMerge];
+};
+
+// Row copies between [B, S, H, D] views of one dtype: job j copies rows
+// [0, rows) of src[j] to dst[j]; all jobs share the strides.
+struct CopyLaunch {
+  const void* src[kMaxMerge];
+  void* dst[kMaxMerge];
+  int32_t n_jobs;
+  int32_t elem_bytes;
+  int32_t B, rows, H, D;
+  int64_t s_sb, s_ss, s_sh;  // element strides
+  int64_t d_sb, d_ss, d_sh;
 };
 
 // Launchers return hipSuccess or the launch error.
@@ -98,6 +118,7 @@ hipError_t launch_partial_f32(const PartialLaunch& a, int D, int n_qtiles, hipSt
 hipError_t launch_merge(const MergeLaunch& a, hipStream_t s);
 hipError_t launch_ring_merge(const RingMergeLaunch& a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeLaunch& a, int D, hipStream_t s);
+hipError_t launch_copy(const CopyLaunch& a, hipStream_t s);
 
 hipError_t cu_count(int* out);  // compute units of the current device (cached, thread-safe)
 

@@ -87,14 +87,16 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeLaunch a) {
     a.out_lse[b * a.ol_sb + s * a.ol_ss + h * a.ol_sh] = (den > 0.f) ? M + fast_log2(den) * kLn2 : kNegInf;
 }
 
-// The c-th partial to reach owner i: Pass-KV sends K/V down the ring, so at
-// step s owner i holds kv chunk (i - s) mod P; Pass-Q sends Q, so at step s
-// the rank holding kv chunk (i + s) mod P computes owner i's piece.  Under
-// the causal mask only kv <= i exists: Pass-KV sees i, i-1, ..., 0 and
-// Pass-Q sees i, then 0, 1, ..., i-1.
-__device__ __forceinline__ int arrival_kv(const RingMergeLaunch& a, int i, int c) {
-  if (a.causal) return a.pass_q ? (c == 0 ? i : c - 1) : i - c;
-  return a.pass_q ? (i + c) % a.P : (i - c + a.P) % a.P;
+// The c-th partial to reach owner i, whose visible K/V chunks are [0, n)
+// (n >= i + 1: a Q chunk always sees its own K/V chunk).  Pass-KV sends K/V
+// down the ring, so at step s owner i holds K/V chunk (i - s) mod P: the
+// visible ones arrive as i, i-1, ..., 0, then n-1, n-2, ..., i+1.  Pass-Q
+// sends Q, so at step s the rank holding K/V chunk (i + s) mod P computes
+// owner i's piece: i, i+1, ..., n-1, then 0, 1, ..., i-1.  (Equal Q and K/V
+// lengths under the causal mask give n = i + 1.)
+__device__ __forceinline__ int arrival_kv(bool pass_q, int i, int n, int c) {
+  if (pass_q) return c < n - i ? i + c : c - (n - i);
+  return c <= i ? i - c : n + i - c;
 }
 
 template <int D>
@@ -112,11 +114,9 @@ __global__ __launch_bounds__(256) void ring_merge_kernel(const RingMergeLaunch a
   const int64_t bs = r / a.H;
   const int s = (int)(bs % a.C);
   const int b = (int)(bs / a.C);
-  const int n = a.causal ? i + 1 : a.P;
-  auto slot = [&](int c) -> int64_t {
-    const int kv = arrival_kv(a, i, c);
-    return a.causal ? (int64_t)i * (i + 1) / 2 + kv : (int64_t)i * a.P + kv;
-  };
+  const int n = a.n_vis[i];
+  const int64_t s0 = a.slot0[i];
+  auto slot = [&](int c) -> int64_t { return s0 + arrival_kv(a.pass_q != 0, i, n, c); };
   f32x4 res;
   float M, den;
   merge_row(

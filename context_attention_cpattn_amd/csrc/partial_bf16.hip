@@ -84,13 +84,13 @@ __global__ __launch_bounds__(256) void partial_bf16_kernel(const PartialLaunch a
   const __bf16* qp = static_cast<const __bf16*>(a.q) + b * a.q_sb + h * a.q_sh +
                      (int64_t)it.q_chunk * a.chunk_len * a.q_ss;
   const __bf16* kp = static_cast<const __bf16*>(a.k) + b * a.k_sb + kvh * a.k_sh +
-                     (int64_t)it.kv_chunk * a.chunk_len * a.k_ss;
+                     (int64_t)it.kv_chunk * a.kv_chunk_len * a.k_ss;
   const __bf16* vp = static_cast<const __bf16*>(a.v) + b * a.v_sb + kvh * a.v_sh +
-                     (int64_t)it.kv_chunk * a.chunk_len * a.v_ss;
+                     (int64_t)it.kv_chunk * a.kv_chunk_len * a.v_ss;
   float* op = a.o + it.slot * a.o_slot + b * a.o_sb + h * a.o_sh;
   float* lp = a.lse != nullptr ? a.lse + it.slot * a.l_slot + b * a.l_sb + h * a.l_sh : nullptr;  // LSE optional
   const int64_t qpos0 = a.q_pos0 + (int64_t)it.q_chunk * a.chunk_len;
-  const int64_t kvpos0 = a.kv_pos0 + (int64_t)it.kv_chunk * a.chunk_len;
+  const int64_t kvpos0 = a.kv_pos0 + (int64_t)it.kv_chunk * a.kv_chunk_len;
 
   const int m0 = qt * C::BM;
   const int r0 = m0 + wave * 32;  // first row of this wave
@@ -408,13 +408,13 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
   const __bf16* qp = static_cast<const __bf16*>(a.q) + b * a.q_sb + h * a.q_sh +
                      (int64_t)it.q_chunk * a.chunk_len * a.q_ss;
   const __bf16* kp = static_cast<const __bf16*>(a.k) + b * a.k_sb + kvh * a.k_sh +
-                     (int64_t)it.kv_chunk * a.chunk_len * a.k_ss;
+                     (int64_t)it.kv_chunk * a.kv_chunk_len * a.k_ss;
   const __bf16* vp = static_cast<const __bf16*>(a.v) + b * a.v_sb + kvh * a.v_sh +
-                     (int64_t)it.kv_chunk * a.chunk_len * a.v_ss;
+                     (int64_t)it.kv_chunk * a.kv_chunk_len * a.v_ss;
   float* op = a.o + it.slot * a.o_slot + b * a.o_sb + h * a.o_sh;
   float* lp = a.lse != nullptr ? a.lse + it.slot * a.l_slot + b * a.l_sb + h * a.l_sh : nullptr;  // LSE optional
   const int64_t qpos0 = a.q_pos0 + (int64_t)it.q_chunk * a.chunk_len;
-  const int64_t kvpos0 = a.kv_pos0 + (int64_t)it.kv_chunk * a.chunk_len;
+  const int64_t kvpos0 = a.kv_pos0 + (int64_t)it.kv_chunk * a.kv_chunk_len;
 
   const int dpos = (int)max<int64_t>(-(1 << 30), min<int64_t>(1 << 30, kvpos0 - qpos0));
   const int m0 = qt * BM;
@@ -759,7 +759,21 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
     }
   }
 
-  write_out(SEG && n_tiles > 0 ? (n_tiles - 1) / a.seg_tiles : 0);
+  const int last_seg = SEG && n_tiles > 0 ? (n_tiles - 1) / a.seg_tiles : 0;
+  write_out(last_seg);
+  if constexpr (SEG) {
+    // Segments past this query tile's last visible key hold pairs its rows see
+    // nothing of (queries shorter than K/V put the last chunk's first keys after
+    // the early rows): each gets the empty partial, O = 0 and LSE = -inf.
+    const int n_seg = (Sk + a.seg_tiles * BN - 1) / (a.seg_tiles * BN);
+    if (last_seg + 1 < n_seg) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] = (f32x16){};
+      m = kNegInf;
+      l = 0.f;
+      for (int seg = last_seg + 1; seg < n_seg; ++seg) write_out(seg);
+    }
+  }
 }
 
 }  // namespace

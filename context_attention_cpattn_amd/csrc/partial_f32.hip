@@ -42,13 +42,13 @@ __global__ __launch_bounds__(256) void partial_f32_kernel(const PartialLaunch a,
   const float* qp = static_cast<const float*>(a.q) + b * a.q_sb + h * a.q_sh +
                     (int64_t)it.q_chunk * a.chunk_len * a.q_ss;
   const float* kp = static_cast<const float*>(a.k) + b * a.k_sb + kvh * a.k_sh +
-                    (int64_t)it.kv_chunk * a.chunk_len * a.k_ss;
+                    (int64_t)it.kv_chunk * a.kv_chunk_len * a.k_ss;
   const float* vp = static_cast<const float*>(a.v) + b * a.v_sb + kvh * a.v_sh +
-                    (int64_t)it.kv_chunk * a.chunk_len * a.v_ss;
+                    (int64_t)it.kv_chunk * a.kv_chunk_len * a.v_ss;
   float* op = a.o + it.slot * a.o_slot + b * a.o_sb + h * a.o_sh;
   float* lp = a.lse != nullptr ? a.lse + it.slot * a.l_slot + b * a.l_sb + h * a.l_sh : nullptr;  // LSE optional
   const int64_t qpos0 = a.q_pos0 + (int64_t)it.q_chunk * a.chunk_len;
-  const int64_t kvpos0 = a.kv_pos0 + (int64_t)it.kv_chunk * a.chunk_len;
+  const int64_t kvpos0 = a.kv_pos0 + (int64_t)it.kv_chunk * a.kv_chunk_len;
 
   const int m0 = qt * ROWS;
   const int row = m0 + tid / T;

@@ -68,7 +68,10 @@ typedef enum cpattn_status {
 
 typedef enum cpattn_dtype { CPATTN_BF16 = 0, CPATTN_F32 = 1 } cpattn_dtype;
 
-typedef enum cpattn_order { CPATTN_PASS_KV = 0, CPATTN_PASS_Q = 1 } cpattn_order;
+/* Ring order.  CPATTN_ORDER_AUTO picks, per call, the order that moves fewer
+ * bytes between ranks (cpattn_ring_select_order).  Calls take the order as an
+ * int holding one of these values; any other value is CPATTN_ERR_INVALID_ARG. */
+typedef enum cpattn_order { CPATTN_PASS_KV = 0, CPATTN_PASS_Q = 1, CPATTN_ORDER_AUTO = 2 } cpattn_order;
 
 typedef struct cpattn_tensor {
   void* data;        /* device pointer (may be NULL only when the tensor is empty) */
@@ -121,84 +124,120 @@ cpattn_status cpattn_merge(const cpattn_tensor* partials, const cpattn_tensor* l
                            cpattn_tensor* out, cpattn_tensor* out_lse, void* stream);
 
 /*
- * cpattn_ring_prefill_workspace_size - bytes of workspace cpattn_ring_prefill
- * needs for this q, chunk count, order and mask (0 if the arguments are
- * invalid; cpattn_last_error() then says why).
+ * Ring layout shared by the ring calls below.
+ *
+ * q [B, Sq, Hq, D] and k, v [B, Skv, Hkv, D] with Sq <= Skv: the queries are
+ * the last Sq positions of the sequence whose keys and values k and v hold
+ * (Sq = Skv is a full prefill; Sq < Skv is new tokens against a cached
+ * context).  Both are cut into n_chunks = P equal contiguous chunks, one per
+ * simulated CP rank (techreport.ngo rewrite, "Context Parallelism for
+ * Million-Token Contexts": the sequence is divided among the ranks): Q chunk
+ * i holds Cq = Sq / P queries at positions Skv - Sq + i Cq + [0, Cq), K/V
+ * chunk j holds Ckv = Skv / P keys at positions j Ckv + [0, Ckv).  Ring step
+ * s gives rank r the pair (Q chunk r, K/V chunk (r - s) mod P) under
+ * CPATTN_PASS_KV, or (Q chunk (r - s) mod P, K/V chunk r) under
+ * CPATTN_PASS_Q (the same section: the two variants differ only in whether
+ * K/V or Q moves between ranks).  Under the causal mask a pair whose first key
+ * lies after its last query sees nothing and is skipped.  Each Q chunk's
+ * partials are merged in the order they reached its owner (Pass-KV: own
+ * chunk, then (i - s) mod P for s = 1, 2, ...; Pass-Q: own chunk, then
+ * (i + s) mod P), skipping the pairs that were skipped.
+ * 1 <= n_chunks <= CPATTN_MAX_MERGE must divide Sq and Skv.
  */
-size_t cpattn_ring_prefill_workspace_size(const cpattn_tensor* q, int n_chunks, cpattn_order order,
-                                          int causal);
 
 /*
- * cpattn_ring_prefill - full-sequence attention by a simulated CP ring.
+ * cpattn_ring_prefill_workspace_size - bytes of workspace cpattn_ring_prefill,
+ * cpattn_ring_step and cpattn_ring_merge need for this q, K/V length, chunk
+ * count and mask: one fp32 O and LSE slot per visible (Q chunk, K/V chunk)
+ * pair.  k may be NULL for K/V as long as q.  Returns 0 if the arguments are
+ * invalid (cpattn_last_error() then says why).
+ */
+size_t cpattn_ring_prefill_workspace_size(const cpattn_tensor* q, const cpattn_tensor* k, int n_chunks, int causal);
+
+/*
+ * cpattn_ring_select_order - the ring order that moves fewer bytes between
+ * ranks for this shape, and the bytes of each.
  *
- * The sequence of q/k/v is cut into n_chunks equal contiguous chunks, chunk
- * c holding tokens [c*C, (c+1)*C) and owned by rank c.  Ring step s gives
- * rank r the pair (Q chunk r, K/V chunk (r - s) mod P) under CPATTN_PASS_KV,
- * or (Q chunk (r - s) mod P, K/V chunk r) under CPATTN_PASS_Q (techreport.ngo
- * rewrite, "Context Parallelism for Million-Token Contexts": the two variants
- * differ only in whether K/V or Q moves between ranks).  Under the causal mask, pairs whose
- * K/V chunk lies after the Q chunk see nothing and are skipped.  All ranks'
- * partials of one step run in one launch; each Q chunk's partials are then
- * merged in the order they reached its owner (Pass-KV: own chunk first, then
- * the earlier chunks in ring order; Pass-Q: own chunk first, then chunks
- * 0, 1, ...).
- *   q   [B, S, Hq, D], k/v [B, S, Hkv, D]  (same S), BF16 or F32
- *   out [B, S, Hq, D]  F32 or BF16
- *   lse [B, S, Hq]     F32, or NULL
+ * The pages present Pass-KV and Pass-Q side by side without a rule
+ * ("Context Parallelism for Million-Token Contexts").  The rule here counts
+ * what a P-rank ring would move: every chunk makes P - 1 hops (K and V of a
+ * chunk under Pass-KV, 2 Ckv Hkv D elements per hop and batch row; a Q chunk
+ * under Pass-Q, Cq Hq D elements), and under Pass-Q every visible pair
+ * computed away from its Q chunk's owner also returns its partial, fp32 O
+ * and LSE (Cq Hq (D + 1) floats).  Elements are q's dtype.  Pass-KV wins
+ * ties.  On return *order is CPATTN_PASS_KV or CPATTN_PASS_Q; the byte counts
+ * are written where the pointers are not NULL.  No device call is made.
+ */
+cpattn_status cpattn_ring_select_order(const cpattn_tensor* q, const cpattn_tensor* k, int n_chunks, int causal,
+                                       int* order, uint64_t* bytes_pass_kv, uint64_t* bytes_pass_q);
+
+/*
+ * cpattn_ring_prefill - attention of every query over the whole sequence by a
+ * simulated CP ring (layout above).
+ *
+ * All ranks' partials of every step go out together (on one device the pairs
+ * are independent), each into its workspace slot; then every Q chunk's
+ * partials are merged in arrival order.
+ *   q [B, Sq, Hq, D], k/v [B, Skv, Hkv, D]  BF16 or F32
+ *   order              CPATTN_PASS_KV, CPATTN_PASS_Q or CPATTN_ORDER_AUTO
+ *   out [B, Sq, Hq, D] F32 or BF16
+ *   lse [B, Sq, Hq]    F32, or NULL
  *   workspace          device buffer of at least
- *                      cpattn_ring_prefill_workspace_size(q, n_chunks, order, causal) bytes
- * n_chunks >= 1 must divide S.
+ *                      cpattn_ring_prefill_workspace_size(q, k, n_chunks, causal) bytes
  */
 cpattn_status cpattn_ring_prefill(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
-                                  int n_chunks, cpattn_order order, int causal,
+                                  int n_chunks, int order /* cpattn_order */, int causal,
                                   cpattn_tensor* out, cpattn_tensor* lse,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * cpattn_ring_step - the partial-attention work of one ring step for every
- * simulated rank: the pairs that step s assigns (as in cpattn_ring_prefill)
- * are computed in one launch into their workspace slots.  Running steps
- * 0 .. n_chunks-1 and then cpattn_ring_merge on the same workspace is exactly
- * cpattn_ring_prefill; on a real CP ring this is what a rank does between two
- * K/V (or Q) exchanges ("Context Parallelism for Million-Token Contexts").
- * Arguments as in cpattn_ring_prefill; 0 <= step < n_chunks.  A step with no
- * causally visible pair enqueues nothing.
+ * simulated rank: the pairs that step s assigns are computed in one launch
+ * into their workspace slots.  Running steps 0 .. n_chunks-1 and then
+ * cpattn_ring_merge on the same workspace is exactly cpattn_ring_prefill; on
+ * a real CP ring this is what a rank does between two K/V (or Q) exchanges
+ * ("Context Parallelism for Million-Token Contexts").  Arguments as in
+ * cpattn_ring_prefill; 0 <= step < n_chunks.  A step with no visible pair
+ * enqueues nothing.
  */
 cpattn_status cpattn_ring_step(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
-                               int n_chunks, cpattn_order order, int causal, int step,
+                               int n_chunks, int order /* cpattn_order */, int causal, int step,
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * cpattn_ring_step_accumulate - one ring step whose partials are merged into
  * the running result as they arrive, with no workspace and no separate merge:
  * the kernel that computes a pair's partial (O, LSE) combines it with the
- * owner's rows already in out/lse by the exact LSE merge (techreport.ngo
- * rewrite, "Context Parallelism for Million-Token Contexts": the per-pair
- * partial results are accumulated into the full attention result).  Step 0
- * gives every owner its first pair (its own chunk) and writes those rows;
- * each later step merges the pair it assigns into them.  Running steps
+ * owner's rows already in out/lse by the exact LSE merge (soumitrasaha.com
+ * reader notes, "The communication bottleneck across all three axes": the
+ * pieces passed around the ring are accumulated into the full result).
+ * Step 0 gives every owner its first pair (its own chunk) and writes those
+ * rows; each later step merges the pair it assigns into them.  Running steps
  * 0 .. n_chunks-1 in order on one stream leaves the full attention in out and
- * lse, merged in arrival order (the order cpattn_ring_merge uses); rows of an
- * owner with no pair at a step are not touched.
+ * lse, merged in arrival order; rows of an owner with no pair at a step are
+ * not touched.
  *   q, k, v, n_chunks, order, causal, step  as in cpattn_ring_step
- *   out [B, S, Hq, D]  F32 (read and written from step 1 on)
- *   lse [B, S, Hq]     F32, required (the running LSE)
+ *   out [B, Sq, Hq, D]  F32 (read and written from step 1 on)
+ *   lse [B, Sq, Hq]     F32, required (the running LSE)
  * Steps after 0 read out/lse as left by the earlier steps of the same ring:
  * calls for one ring must not overlap, and nothing else may write out/lse in
  * between.
  */
 cpattn_status cpattn_ring_step_accumulate(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
-                                          int n_chunks, cpattn_order order, int causal, int step,
+                                          int n_chunks, int order /* cpattn_order */, int causal, int step,
                                           cpattn_tensor* out, cpattn_tensor* lse, void* stream);
 
 /*
  * cpattn_ring_merge - merge every Q chunk's partials from a workspace filled
  * by cpattn_ring_step (all steps), in the order they reached the chunk's
- * owner, into out [B, S, Hq, D] (F32 or BF16) and lse [B, S, Hq] (F32, or
- * NULL).  The shapes come from out; n_chunks, order and causal must match the
- * steps that filled the workspace.
+ * owner, into out [B, Sq, Hq, D] (F32 or BF16) and lse [B, Sq, Hq] (F32, or
+ * NULL).  The query shapes come from out; kv_len is the K/V length Skv the
+ * steps ran with.  n_chunks, causal and the order must match the steps that
+ * filled the workspace; the order must be CPATTN_PASS_KV or CPATTN_PASS_Q
+ * (for steps run with CPATTN_ORDER_AUTO, the order
+ * cpattn_ring_select_order returns).
  */
-cpattn_status cpattn_ring_merge(int n_chunks, cpattn_order order, int causal,
+cpattn_status cpattn_ring_merge(int n_chunks, int order /* cpattn_order */, int causal, int64_t kv_len,
                                 const void* workspace, size_t workspace_bytes,
                                 cpattn_tensor* out, cpattn_tensor* lse, void* stream);
 
@@ -209,13 +248,13 @@ cpattn_status cpattn_ring_merge(int n_chunks, cpattn_order order, int causal,
  * K/V chunks reach it, instead of being stored and merged afterwards (the
  * pieces gathered around the ring accumulated into the full result: "The
  * communication bottleneck across all three axes", soumitrasaha.com reader
- * notes).  On one device the owner of Q chunk i sees the keys [0, (i+1)C)
- * (all of them without the causal mask) in one pass, in position order;
+ * notes).  On one device the owner of Q chunk i sees the keys up to its last
+ * query (all of them without the causal mask) in one pass, in position order;
  * any order of the same keys is exact up to rounding, so the result equals
  * cpattn_ring_prefill's within rounding.  No workspace, one launch.
- *   q, k, v  as for cpattn_ring_prefill
- *   out      [B, S, Hq, D] F32
- *   lse      [B, S, Hq] F32, or NULL to skip
+ *   q, k, v  as for cpattn_ring_prefill (Sq <= Skv)
+ *   out      [B, Sq, Hq, D] F32
+ *   lse      [B, Sq, Hq] F32, or NULL to skip
  * Errors as for cpattn_ring_prefill (out must be F32).
  */
 cpattn_status cpattn_ring_prefill_fused(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
@@ -249,10 +288,70 @@ cpattn_status cpattn_splitkv_decode(const cpattn_tensor* q, const cpattn_tensor*
                                     int n_chunks, cpattn_tensor* out, cpattn_tensor* lse,
                                     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * cpattn_kv_cache_write - the prefill's K/V, chunk by chunk, into the KV-cache
+ * shards of the CP ranks.
+ *
+ * The prefill constructs the KV cache of every transformer layer and decode
+ * then reads and extends it (techreport.ngo rewrite, "Why Parallelism Defines
+ * LLM Serving Cost"); with the sequence divided among CP ranks ("Context
+ * Parallelism for Million-Token Contexts"), rank r keeps its own chunk's keys
+ * and values.  Rows [0, C) of shard r receive rows [r C, (r+1) C) of k and v
+ * (C = S / n_chunks); the other shard rows are not touched.
+ *   k, v                 [B, S, Hkv, D] BF16 or F32
+ *   k_shards, v_shards   host arrays of n_chunks descriptors [B, cap, Hkv, D]
+ *                        (same dtype, shape and strides; only the pointers
+ *                        differ), cap >= C
+ * 1 <= n_chunks <= CPATTN_MAX_MERGE must divide S.  A byte copy.
+ */
+cpattn_status cpattn_kv_cache_write(const cpattn_tensor* k, const cpattn_tensor* v, int n_chunks,
+                                    const cpattn_tensor* k_shards, const cpattn_tensor* v_shards, void* stream);
+
+/*
+ * cpattn_kv_cache_append - new tokens' keys and values into rows
+ * [row, row + T) of one shard (the cache growing by decode, same sections).
+ *   k_new, v_new       [B, T, Hkv, D]
+ *   k_shard, v_shard   [B, cap, Hkv, D], same dtype; 0 <= row, row + T <= cap
+ * A byte copy.
+ */
+cpattn_status cpattn_kv_cache_append(const cpattn_tensor* k_new, const cpattn_tensor* v_new,
+                                     const cpattn_tensor* k_shard, const cpattn_tensor* v_shard, int64_t row,
+                                     void* stream);
+
+/*
+ * cpattn_cp_decode_workspace_size - bytes of workspace cpattn_cp_decode needs
+ * for this q and these shards (sized by the shards' capacity, so it does not
+ * change as they fill); 0 if the arguments are invalid.
+ */
+size_t cpattn_cp_decode_workspace_size(const cpattn_tensor* q, const cpattn_tensor* k_shards, int n_shards);
+
+/*
+ * cpattn_cp_decode - one new token per sequence against a KV cache sharded
+ * across CP ranks.
+ *
+ * Decode reads the KV cache and is memory-bandwidth bound ("Why Parallelism
+ * Defines LLM Serving Cost"); with the cache divided among the ranks, each
+ * rank attends the new query against its own shard and the per-rank partials
+ * are merged by the exact LSE rule.  The new token comes after every cached
+ * key, so it sees all of them.  Shard r contributes its rows
+ * [0, shard_len[r]); shards are merged in index order.
+ *   q                    [B, 1, Hq, D] BF16
+ *   k_shards, v_shards   host arrays of n_shards descriptors [B, cap, Hkv, D]
+ *                        BF16 (same shape and strides), Hq / Hkv <= 64
+ *   shard_len            host array of n_shards lengths, 0 <= len <= cap
+ *   out [B, 1, Hq, D]    F32 or BF16;  lse [B, 1, Hq] F32, or NULL
+ *   workspace            >= cpattn_cp_decode_workspace_size(q, k_shards, n_shards)
+ * 1 <= n_shards <= CPATTN_MAX_MERGE.  A row whose shards are all empty gets
+ * out = 0 and lse = -inf.
+ */
+cpattn_status cpattn_cp_decode(const cpattn_tensor* q, const cpattn_tensor* k_shards, const cpattn_tensor* v_shards,
+                               const int64_t* shard_len, int n_shards, cpattn_tensor* out, cpattn_tensor* lse,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* cpattn_last_error(void);
 
-/* Library version string, e.g. "cpattn 0.1.0 gfx950". */
+/* Library version string, e.g. "cpattn 0.2.0 gfx950". */
 const char* cpattn_version(void);
 
 #ifdef __cplusplus

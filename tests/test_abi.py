@@ -34,10 +34,17 @@ def test_exports_every_declared_symbol():
     syms = header_symbols()
     assert {"cpattn_partial", "cpattn_merge", "cpattn_ring_prefill", "cpattn_ring_prefill_workspace_size",
             "cpattn_splitkv_decode", "cpattn_splitkv_decode_workspace_size", "cpattn_last_error",
-            "cpattn_version"} <= set(syms)
+            "cpattn_version", "cpattn_ring_select_order", "cpattn_kv_cache_write", "cpattn_kv_cache_append",
+            "cpattn_cp_decode", "cpattn_cp_decode_workspace_size"} <= set(syms)
     raw = ctypes.CDLL(cp.LIB_PATH)
     for s in syms:
         assert hasattr(raw, s), f"{s} declared in cpattn.h but not exported"
+    # and nothing else: every exported cpattn_ symbol is declared
+    import subprocess
+    nm = subprocess.run(["nm", "-D", "--defined-only", cp.LIB_PATH], capture_output=True, text=True)
+    if nm.returncode == 0:
+        exported = set(re.findall(r"\bT (cpattn_\w+)", nm.stdout))
+        assert exported == set(syms), exported ^ set(syms)
 
 
 def test_version():
@@ -130,8 +137,9 @@ def test_merge_validation():
     assert lib.cpattn_merge(P4, L, 1, r(bshd(1, 8, 2, 32, cp.DT_F32)), None, None) == cp.ERR_UNSUPPORTED
 
 
-def ring_ws(q, n, order=0, causal=1):
-    return lib.cpattn_ring_prefill_workspace_size(ctypes.byref(q), n, order, causal)
+def ring_ws(q, n, causal=1, k=None):
+    return lib.cpattn_ring_prefill_workspace_size(ctypes.byref(q), ctypes.byref(k) if k is not None else None, n,
+                                                  causal)
 
 
 def test_ring_workspace_size_formula():
@@ -142,11 +150,64 @@ def test_ring_workspace_size_formula():
     l = n_items * 8192 * 16 * 4
     up = lambda x: (x + 255) // 256 * 256
     assert ring_ws(q, 16) == up(o) + up(l)
+    assert ring_ws(q, 16, k=bshd(1, 131072, 1, 128)) == up(o) + up(l)
     assert ring_ws(q, 16, causal=0) == up(256 * 8192 * 16 * 128 * 4) + up(256 * 8192 * 16 * 4)
-    assert ring_ws(q, 16, order=1) == ring_ws(q, 16, order=0)
     assert ring_ws(q, 3) == 0 and "divide" in err()
     assert ring_ws(q, 0) == 0
-    assert ring_ws(q, 16, order=5) == 0
+    assert ring_ws(q, 16, causal=5) == 0
+    # K/V shorter than Q is refused; longer K/V must also divide into the chunks
+    assert ring_ws(q, 16, k=bshd(1, 65536, 1, 128)) == 0 and "at least as long" in err()
+    assert ring_ws(q, 16, k=bshd(1, 131080, 1, 128)) == 0
+
+
+@pytest.mark.parametrize("Sq,Skv,P", [(2048, 133120, 16), (2048, 4096, 4), (96, 960, 3), (512, 512, 8),
+                                      (64, 64 * 40, 64), (256, 1024, 1)])
+def test_ring_workspace_slots_are_the_oracles_visible_pairs(Sq, Skv, P):
+    """Queries shorter than K/V: one slot per pair the oracle's schedule visits (its visibility is
+    decided from positions)."""
+    import oracle
+    q, k = bshd(1, Sq, 2, 64), bshd(1, Skv, 1, 64)
+    up = lambda x: (x + 255) // 256 * 256
+    for causal in (1, 0):
+        n = sum(len(st) for st in oracle.schedule(P, oracle.PASS_KV, bool(causal), Sq, Skv))
+        C = Sq // P
+        assert ring_ws(q, P, causal, k) == up(n * C * 2 * 64 * 4) + up(n * C * 2 * 4)
+
+
+def select(q, k, n, causal=1):
+    order, bkv, bq = ctypes.c_int(-1), ctypes.c_uint64(), ctypes.c_uint64()
+    st = lib.cpattn_ring_select_order(ctypes.byref(q), ctypes.byref(k), n, causal, ctypes.byref(order),
+                                      ctypes.byref(bkv), ctypes.byref(bq))
+    return st, order.value, bkv.value, bq.value
+
+
+@pytest.mark.parametrize("shape", [(1, 131072, 131072, 16, 1, 128, 16), (1, 2048, 133120, 16, 1, 128, 16),
+                                   (2, 512, 512, 8, 8, 64, 8), (3, 96, 960, 4, 2, 64, 3), (1, 64, 8192, 32, 8, 128, 4),
+                                   (4, 1024, 4096, 16, 4, 128, 2), (1, 8, 8, 2, 1, 64, 1), (1, 4, 64, 64, 1, 128, 4)])
+@pytest.mark.parametrize("dt", [cp.DT_BF16, cp.DT_F32])
+def test_select_order_matches_the_oracle_walk(shape, dt):
+    """The library's closed-form byte counts and choice equal the oracle's step-by-step walk of the
+    ring (no device call is made)."""
+    import oracle
+    B, Sq, Skv, Hq, Hkv, D, P = shape
+    e = 2 if dt == cp.DT_BF16 else 4
+    for causal in (1, 0):
+        st, order, bkv, bq = select(bshd(B, Sq, Hq, D, dt), bshd(B, Skv, Hkv, D, dt), P, causal)
+        assert st == cp.OK
+        assert bkv == oracle.exchange_bytes(P, oracle.PASS_KV, bool(causal), B, Sq, Skv, Hq, Hkv, D, e)
+        assert bq == oracle.exchange_bytes(P, oracle.PASS_Q, bool(causal), B, Sq, Skv, Hq, Hkv, D, e)
+        want = oracle.select_order(P, bool(causal), B, Sq, Skv, Hq, Hkv, D, e)
+        assert order == (cp.PASS_Q if want == oracle.PASS_Q else cp.PASS_KV)
+
+
+def test_select_order_validation():
+    q, k = bshd(1, 512, 4, 64), bshd(1, 1024, 1, 64)
+    assert select(q, k, 4)[0] == cp.OK
+    assert select(q, k, 3)[0] == cp.ERR_INVALID_ARG
+    assert select(q, bshd(1, 256, 1, 64), 4)[0] == cp.ERR_INVALID_ARG
+    assert select(q, bshd(1, 1024, 3, 64), 4)[0] == cp.ERR_INVALID_ARG
+    assert select(q, bshd(1, 1024, 1, 64, cp.DT_F32), 4)[0] == cp.ERR_INVALID_ARG
+    assert lib.cpattn_ring_select_order(ctypes.byref(q), ctypes.byref(k), 4, 1, None, None, None) == cp.ERR_INVALID_ARG
 
 
 def test_decode_workspace_size():
@@ -173,7 +234,8 @@ def test_ring_validation():
     assert need > 0
 
     def call(n=4, order=0, causal=1, ws=FAKE, nbytes=None, k_=k, out_=out):
-        return lib.cpattn_ring_prefill(r(q), r(k_), r(v), n, order, causal, r(out_), r(lse), ws,
+        v_ = bshd(k_.B, k_.S, k_.H, k_.D, k_.dtype)  # v shaped like k
+        return lib.cpattn_ring_prefill(r(q), r(k_), r(v_), n, order, causal, r(out_), r(lse), ws,
                                        need if nbytes is None else nbytes, None)
 
     assert call(n=3) == cp.ERR_INVALID_ARG
@@ -184,8 +246,20 @@ def test_ring_validation():
     assert call(ws=None) == cp.ERR_WORKSPACE
     assert call(nbytes=need - 1) == cp.ERR_WORKSPACE and "needed" in err()
     assert call(ws=FAKE + 4) == cp.ERR_WORKSPACE
-    assert call(k_=bshd(1, 256, 1, 64)) == cp.ERR_INVALID_ARG
+    assert call(k_=bshd(1, 256, 1, 64)) == cp.ERR_INVALID_ARG and "at least as long" in err()
+    assert call(k_=bshd(1, 514, 1, 64)) == cp.ERR_INVALID_ARG and "divisible" in err()
     assert call(out_=bshd(1, 512, 4, 64, dt=7)) == cp.ERR_INVALID_ARG
+    assert call(order=3) == cp.ERR_INVALID_ARG
+
+    def merge(n=4, order=0, causal=1, kv_len=512, nbytes=None, out_=out):
+        return lib.cpattn_ring_merge(n, order, causal, kv_len, FAKE, need if nbytes is None else nbytes, r(out_),
+                                     r(lse), None)
+
+    assert merge(order=cp.ORDER_AUTO) == cp.ERR_INVALID_ARG  # the merge needs the order the steps ran in
+    assert merge(kv_len=256) == cp.ERR_INVALID_ARG
+    assert merge(kv_len=514) == cp.ERR_INVALID_ARG
+    assert merge(nbytes=need - 1) == cp.ERR_WORKSPACE
+    assert merge(kv_len=1024) == cp.ERR_WORKSPACE  # a longer K/V has more visible pairs than `need` holds
 
 
 @no_gpu
@@ -236,6 +310,57 @@ def test_decode_validation():
     assert call(nbytes=need - 16) == cp.ERR_WORKSPACE
     assert call(q_=bshd(4, 1, 128, 128)) in (cp.ERR_INVALID_ARG, cp.ERR_UNSUPPORTED)
     assert lib.cpattn_splitkv_decode_workspace_size(r(q), r(k), 3) == 0
+
+
+def shards(n, B, cap, H, D, dt=cp.DT_BF16, step=1 << 20):
+    return (T * n)(*[bshd(B, cap, H, D, dt, ptr=FAKE + r * step) for r in range(n)])
+
+
+@no_gpu
+def test_kv_cache_validation():
+    r = ctypes.byref
+    k, v = bshd(2, 1024, 1, 128), bshd(2, 1024, 1, 128)
+    ks, vs = shards(4, 2, 300, 1, 128), shards(4, 2, 300, 1, 128)
+    w = lambda k_=k, v_=v, n=4, ks_=ks, vs_=vs: lib.cpattn_kv_cache_write(r(k_), r(v_), n, ks_, vs_, None)
+    assert w(n=3) == cp.ERR_INVALID_ARG and "divisible" in err()
+    assert w(n=0) == cp.ERR_INVALID_ARG
+    assert w(n=65) == cp.ERR_UNSUPPORTED
+    assert w(ks_=shards(4, 2, 200, 1, 128), vs_=shards(4, 2, 200, 1, 128)) == cp.ERR_INVALID_ARG and "chunk" in err()
+    assert w(ks_=shards(4, 2, 300, 2, 128), vs_=shards(4, 2, 300, 2, 128)) == cp.ERR_INVALID_ARG
+    assert w(ks_=shards(4, 2, 300, 1, 128, cp.DT_F32), vs_=shards(4, 2, 300, 1, 128, cp.DT_F32)) == cp.ERR_INVALID_ARG
+    mixed = shards(4, 2, 300, 1, 128)
+    mixed[2].S = 301
+    assert w(ks_=mixed) == cp.ERR_INVALID_ARG and "shard 2" in err()
+    assert lib.cpattn_kv_cache_write(r(k), r(v), 4, None, vs, None) == cp.ERR_INVALID_ARG
+    kn, vn = bshd(2, 3, 1, 128), bshd(2, 3, 1, 128)
+    a = lambda row, kn_=kn: lib.cpattn_kv_cache_append(r(kn_), r(vn), r(ks[0]), r(vs[0]), row, None)
+    assert a(298) == cp.ERR_INVALID_ARG and "fit" in err()
+    assert a(-1) == cp.ERR_INVALID_ARG
+    assert a(0, kn_=bshd(2, 3, 2, 128)) == cp.ERR_INVALID_ARG
+
+
+@no_gpu
+def test_cp_decode_validation():
+    r = ctypes.byref
+    q = bshd(3, 1, 16, 128)
+    ks, vs = shards(4, 3, 2048, 1, 128), shards(4, 3, 2048, 1, 128)
+    need = lib.cpattn_cp_decode_workspace_size(r(q), ks, 4)
+    assert need > 0
+    out = bshd(3, 1, 16, 128, cp.DT_F32)
+
+    def call(lens=(2048, 10, 0, 7), q_=q, n=4, nbytes=need, ks_=ks, vs_=vs):
+        arr = (ctypes.c_int64 * len(lens))(*lens)
+        return lib.cpattn_cp_decode(r(q_), ks_, vs_, arr, n, r(out), None, FAKE, nbytes, None)
+
+    assert call(lens=(2049, 10, 0, 7)) == cp.ERR_INVALID_ARG and "shard 0" in err()
+    assert call(lens=(5, -1, 0, 7)) == cp.ERR_INVALID_ARG
+    assert call(nbytes=need - 16) == cp.ERR_WORKSPACE
+    assert call(q_=bshd(3, 2, 16, 128)) == cp.ERR_INVALID_ARG
+    assert call(n=0) == cp.ERR_INVALID_ARG
+    assert call(ks_=shards(4, 3, 2048, 1, 64), vs_=shards(4, 3, 2048, 1, 64)) == cp.ERR_INVALID_ARG
+    assert lib.cpattn_cp_decode(r(q), ks, vs, None, 4, r(out), None, FAKE, need, None) == cp.ERR_INVALID_ARG
+    # the workspace is sized by capacity, so filling the shards never changes it
+    assert lib.cpattn_cp_decode_workspace_size(r(q), shards(4, 3, 4096, 1, 128), 4) >= need
 
 
 def test_last_error_cleared_by_success():

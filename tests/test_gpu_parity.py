@@ -299,8 +299,13 @@ def _sampled_check(cp, w, o, l, q, k, v, name):
     compare(o.index_select(1, idx), l.index_select(1, idx), o_ref, l_ref, BF16_TOL, name + " (64 sampled rows)")
 
 
-def test_workload_128k_both_orders(cp):
+@pytest.fixture(scope="module")
+def c4(cp):
+    """The 128K-token workload through every ring path once: whole ring prefills in both orders, the
+    per-step launches bench.py times, the accumulating ring steps and the fused prefill.  Checks
+    among the paths run here; the comparisons with the oracle are the tests below."""
     w = si.WORKLOADS["prefill_bf16_s128k_p16"]
+    banner(w.name, "drawing inputs")
     q, k, v = si.make_qkv(w)
     gq, gk, gv = q.to(DEV), k.to(DEV), v.to(DEV)
     res = {}
@@ -308,11 +313,10 @@ def test_workload_128k_both_orders(cp):
         banner(w.name, order, w.n_chunks)
         res[order] = cp.ring_prefill(gq, gk, gv, w.n_chunks, order, True)
         torch.cuda.synchronize()
-        _sampled_check(cp, w, *res[order], q, k, v, f"{w.name} {order}")
     # the launch configuration bench.py times: one ring_step launch per step, then ring_merge;
     # every pair is computed by the same per-block code, so the result is bit-identical
     banner(w.name, "pass_kv per-step launches")
-    ws = torch.empty(cp.ring_prefill_workspace_size(gq, w.n_chunks, "pass_kv", True), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(cp.ring_prefill_workspace_size(gq, w.n_chunks, True), dtype=torch.uint8, device=DEV)
     o_s = torch.empty_like(res["pass_kv"][0])
     l_s = torch.empty_like(res["pass_kv"][1])
     for step in range(w.n_chunks):
@@ -326,29 +330,25 @@ def test_workload_128k_both_orders(cp):
     d_l = (lkv - lq).abs().max().item()
     print(f"[parity] {w.name}: pass_kv vs pass_q max|dO|={d_o:.3e} max|dLSE|={d_l:.3e}", flush=True)
     assert d_o <= 1e-5 and d_l <= 1e-5
-    del oq, lq
     # the accumulating ring steps (each partial merged into the running result by the kernel that
-    # computes it): same sampled rows against the oracle, every row against the per-pair path
+    # computes it), in the order bench.py times them
     banner(w.name, "ring_step_accumulate", w.n_chunks)
     oa = torch.empty_like(okv)
     la = torch.empty_like(lkv)
     for step in range(w.n_chunks):
         cp.ring_step_accumulate(gq, gk, gv, w.n_chunks, step, oa, la, "pass_kv", True)
     torch.cuda.synchronize()
-    _sampled_check(cp, w, oa, la, q, k, v, f"{w.name} accumulate")
     d_o = (okv - oa).abs().max().item()
     d_l = (lkv - la).abs().max().item()
     print(f"[parity] {w.name}: accumulate vs pass_kv max|dO|={d_o:.3e} max|dLSE|={d_l:.3e}", flush=True)
     assert d_o <= 1e-5 and d_l <= 1e-5
-    del oa, la
-    # the fused ring prefill (online merge, one launch): the same sampled rows against the oracle,
-    # and every row against the per-pair path.  The two round P to bf16 against different running
-    # maxima, so they differ by bf16 rounding of P, not by fp32 reordering alone: the bar between
-    # them is the bf16 tolerance each already meets against the oracle.
+    res["accumulate"] = (oa, la)
+    # the fused ring prefill (online merge, one launch).  It and the per-pair path round P to bf16
+    # against different running maxima, so they differ by bf16 rounding of P, not by fp32
+    # reordering alone: the bar between them is the bf16 tolerance each meets against the oracle.
     banner(w.name, "ring_prefill_fused", w.n_chunks)
     of, lf = cp.ring_prefill_fused(gq, gk, gv, w.n_chunks, True)
     torch.cuda.synchronize()
-    _sampled_check(cp, w, of, lf, q, k, v, f"{w.name} fused")
     d = (okv - of).abs_()
     d_o, m_o = d.max().item(), d.mean().item()
     del d
@@ -356,8 +356,45 @@ def test_workload_128k_both_orders(cp):
     print(f"[parity] {w.name}: fused vs pass_kv max|dO|={d_o:.3e} mean|dO|={m_o:.3e} max|dLSE|={d_l:.3e}",
           flush=True)
     assert d_o <= BF16_TOL.max_abs and m_o <= BF16_TOL.mean_abs and d_l <= BF16_TOL.lse_abs
-    # properties over every row: finite output, LSE within its possible range
-    assert torch.isfinite(okv).all() and torch.isfinite(lkv).all()
+    res["fused"] = (of, lf)
+    for name, (o_, l_) in res.items():  # every row: finite output
+        assert torch.isfinite(o_).all() and torch.isfinite(l_).all(), name
+    del gq, gk, gv
+    yield w, q, k, v, res
+    del res
+    torch.cuda.empty_cache()
+
+
+C4_PATHS = ["pass_kv", "pass_q", "accumulate", "fused"]
+
+
+@pytest.mark.parametrize("path", C4_PATHS)
+def test_workload_128k_sampled_rows(cp, c4, path):
+    """All owners: 64 sampled rows per head (first and last token, both sides of every chunk
+    boundary, 30 drawn) against the oracle at full causal context."""
+    w, q, k, v, res = c4
+    _sampled_check(cp, w, *res[path], q, k, v, f"{w.name} {path}")
+
+
+# Owner chunks 0 (the first 8192 rows, one pair each) and 15 (the last 8192 rows, which merge all
+# 16 pairs and see the longest context) are compared with the oracle at every row and head, in
+# parts of 1024 rows so each part's fp64 oracle (~1e12 FLOP at most) finishes in seconds.
+C4_PARTS = [(0, r0) for r0 in range(0, 8192, 1024)] + [(15, 15 * 8192 + r0) for r0 in range(0, 8192, 1024)]
+
+
+@pytest.mark.parametrize("owner,r0", C4_PARTS, ids=lambda x: str(x))
+def test_workload_128k_owner_rows(cp, c4, owner, r0):
+    import time
+
+    w, q, k, v, res = c4
+    r1 = r0 + 1024
+    t0 = time.perf_counter()
+    banner(w.name, f"oracle rows {r0}..{r1 - 1} (owner {owner})")
+    o_ref, l_ref = oracle.partial_attention(q[:, r0:r1], k[:, :r1], v[:, :r1], r0, 0, True, row_block=256)
+    print(f"[oracle] {w.name} rows {r0}..{r1 - 1}: {time.perf_counter() - t0:.1f} s", flush=True)
+    for path in C4_PATHS:
+        o, l = res[path]
+        compare(o[:, r0:r1], l[:, r0:r1], o_ref, l_ref, BF16_TOL, f"{w.name} {path} owner {owner} rows {r0}..{r1 - 1}")
 
 
 @pytest.mark.timeout(900)

@@ -175,3 +175,29 @@ def test_decode_after_prefill_matches_last_row(cp):
         d_o = (x - od).abs().max().item()
         d_l = (y - ld).abs().max().item()
         assert d_o <= BF16_TOL.max_abs and d_l <= BF16_TOL.lse_abs, (name, d_o, d_l)
+
+
+def test_side_stream_buffers_survive_reuse(cp):
+    """Calls on a side stream allocate their workspace and outputs on torch's current stream; the
+    binding must keep the caching allocator from handing those blocks to work queued on the default
+    stream while the side stream's kernels still use them.  Each call is followed at once by large
+    allocations filled on the default stream before the side stream is waited for."""
+    S, P = 4096, 4
+    q, k, v = qkv(31, S, 8, 1, 128)
+    qd = si.draw_tensor(32, 0, (16, 1, 16, 128), torch.bfloat16).to(DEV)
+    kd = si.draw_tensor(32, 1, (16, 8192, 1, 128), torch.bfloat16).to(DEV)
+    vd = si.draw_tensor(32, 2, (16, 8192, 1, 128), torch.bfloat16).to(DEV)
+    o_ref, l_ref = oracle.full_attention(q.cpu(), k.cpu(), v.cpu(), True)
+    od_ref, ld_ref = oracle.splitkv_decode(qd.cpu(), kd.cpu(), vd.cpu(), 8)
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    banner("side stream", "ring_prefill + splitkv_decode")
+    o, l = cp.ring_prefill(q, k, v, P, "pass_kv", True, stream=side)
+    junk = [torch.full((1 << 26,), 7.0, device=DEV) for _ in range(4)]  # 1 GiB of fills on the default stream
+    od, ld = cp.splitkv_decode(qd, kd, vd, 8, stream=side.cuda_stream)  # a raw handle works too
+    junk += [torch.full((1 << 26,), -3.0, device=DEV) for _ in range(4)]
+    side.synchronize()
+    torch.cuda.synchronize()
+    compare(o, l, o_ref, l_ref, BF16_TOL, "ring_prefill on a side stream")
+    compare(od, ld, od_ref, ld_ref, BF16_TOL, "splitkv_decode on a side stream")
+    del junk
