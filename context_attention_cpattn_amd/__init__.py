@@ -20,7 +20,7 @@ __all__ = [
     "CpattnError", "Tensor", "LIB_PATH", "version", "describe", "partial", "merge",
     "ring_prefill", "ring_prefill_workspace_size", "ring_prefill_fused", "ring_select_order",
     "ring_step", "ring_step_accumulate", "ring_merge",
-    "splitkv_decode", "splitkv_decode_workspace_size",
+    "splitkv_decode", "splitkv_decode_workspace_size", "splitkv_decode_noalloc",
     "kv_cache_write", "kv_cache_append", "cp_decode", "cp_decode_workspace_size",
     "PASS_KV", "PASS_Q", "ORDER_AUTO", "MAX_MERGE",
 ]
@@ -75,6 +75,7 @@ def _load() -> ctypes.CDLL:
         "cpattn_ring_step_accumulate": ([P, P, P, i32, i32, i32, i32, P, P, vp], i32),
         "cpattn_splitkv_decode_workspace_size": ([P, P, i32], sz),
         "cpattn_splitkv_decode": ([P, P, P, i32, P, P, vp, sz, vp], i32),
+        "cpattn_splitkv_decode_noalloc": ([P, P, P, i32, P, P, vp], i32),
         "cpattn_kv_cache_write": ([P, P, i32, P, P, vp], i32),
         "cpattn_kv_cache_append": ([P, P, P, P, i64, vp], i32),
         "cpattn_cp_decode_workspace_size": ([P, P, i32], sz),
@@ -310,6 +311,15 @@ def splitkv_decode(q, k, v, n_chunks: int, out=None, lse=None, workspace=None, o
     dq, dk, dv, do, dl = describe(q), describe(k), describe(v), describe(out), describe(lse, True)
     _check(lib.cpattn_splitkv_decode(_ref(dq), _ref(dk), _ref(dv), int(n_chunks), _ref(do), _ref(dl),
                                      workspace.data_ptr(), _nbytes(workspace), h))
+    return out, lse
+
+
+def splitkv_decode_noalloc(q, k, v, n_chunks: int, out, lse=None, stream=None):
+    """``splitkv_decode`` with the partials in the library's fixed 64 MiB scratch: the C call
+    allocates nothing (``out``/``lse`` are the caller's).  Calls that overlap on one GPU race."""
+    h, _ = _stream(q, stream)
+    _check(lib.cpattn_splitkv_decode_noalloc(_ref(describe(q)), _ref(describe(k)), _ref(describe(v)), int(n_chunks),
+                                             _ref(describe(out)), _ref(describe(lse, True)), h))
     return out, lse
 
 

@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcpattn.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "partial_bf16.hip", "partial_f32.hip", "merge.hip", "decode.hip", "copy.hip"]
+SOURCES = ["api.cpp", "partial_bf16.hip", "partial_f32.hip", "merge.hip", "decode.hip", "copy.hip", "scratch.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -803,6 +803,31 @@ cpattn_status cpattn_splitkv_decode(const cpattn_tensor* q, const cpattn_tensor*
   return run_decode(*q, *k, *v, n_chunks, kc, vc, len, L, out, lse, workspace, static_cast<hipStream_t>(stream));
 }
 
+cpattn_status cpattn_splitkv_decode_noalloc(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                                            int n_chunks, cpattn_tensor* out, cpattn_tensor* lse, void* stream) {
+  cpattn_status s;
+  if ((s = check_decode(q, k, v, n_chunks)) != CPATTN_OK) return s;
+  if ((s = check_out(out, lse, *q, true, false)) != CPATTN_OK) return s;
+  const int64_t C = k->S / n_chunks;
+  const DecodeLayout L = decode_layout(*q, k->H, C, n_chunks);
+  if (L.bytes > cpattn::kScratchBytes)
+    return fail(CPATTN_ERR_WORKSPACE, "this decode needs %zu bytes of scratch; the fixed scratch holds %zu "
+                "(use cpattn_splitkv_decode with a workspace)", L.bytes, cpattn::kScratchBytes);
+  if (q->B == 0) return ok();
+  void* scratch = nullptr;
+  const hipError_t e = cpattn::scratch_address(&scratch);
+  if (e != hipSuccess) return hip_fail(e, "scratch address lookup");
+  const void* kc[cpattn::kMaxMerge];
+  const void* vc[cpattn::kMaxMerge];
+  int64_t len[cpattn::kMaxMerge];
+  for (int c = 0; c < n_chunks; ++c) {
+    kc[c] = static_cast<const __bf16*>(k->data) + c * C * k->stride_s;
+    vc[c] = static_cast<const __bf16*>(v->data) + c * C * v->stride_s;
+    len[c] = C;
+  }
+  return run_decode(*q, *k, *v, n_chunks, kc, vc, len, L, out, lse, scratch, static_cast<hipStream_t>(stream));
+}
+
 cpattn_status cpattn_kv_cache_write(const cpattn_tensor* k, const cpattn_tensor* v, int n_chunks,
                                     const cpattn_tensor* k_shards, const cpattn_tensor* v_shards, void* stream) {
   cpattn_status s;

@@ -122,6 +122,11 @@ hipError_t launch_copy(const CopyLaunch& a, hipStream_t s);
 
 hipError_t cu_count(int* out);  // compute units of the current device (cached, thread-safe)
 
+// The fixed scratch of cpattn_splitkv_decode_noalloc: kScratchBytes of device
+// memory per GPU, its device address looked up once per device (thread-safe).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+hipError_t scratch_address(void** out);
+
 int partial_bf16_rows_per_block(int D);  // query rows per workgroup of the bf16 kernel
 int partial_f32_rows_per_block(int D);
 

@@ -289,6 +289,25 @@ cpattn_status cpattn_splitkv_decode(const cpattn_tensor* q, const cpattn_tensor*
                                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * cpattn_splitkv_decode_noalloc - cpattn_splitkv_decode for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).
+ *
+ * Same arguments, result and kernels as cpattn_splitkv_decode, but the
+ * partials live in a fixed scratch array inside the library (64 MiB per GPU,
+ * held until the process ends) instead of a caller's workspace; the call
+ * allocates and frees nothing.  A decode whose partials need more than the
+ * scratch holds (cpattn_splitkv_decode_workspace_size() > 64 MiB) returns
+ * CPATTN_ERR_WORKSPACE before any HIP call.  Every call on one GPU shares
+ * that GPU's scratch: calls that overlap on one GPU (other streams, other
+ * host threads) race and must be serialised by the caller.  Nothing in the
+ * scratch needs to start at zero: every partial the merge reads is written
+ * by the same call first.
+ */
+cpattn_status cpattn_splitkv_decode_noalloc(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                                            int n_chunks, cpattn_tensor* out, cpattn_tensor* lse, void* stream);
+
+/*
  * cpattn_kv_cache_write - the prefill's K/V, chunk by chunk, into the KV-cache
  * shards of the CP ranks.
  *
