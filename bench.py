@@ -5,20 +5,21 @@ Headline (``value``): causal prefill attention TFLOP/s (unmasked FLOPs only:
 4 * D * Hq per visible (query, key) pair) on the 128K-token workload --
 1 x 131072 tokens, 16 query heads on 1 KV head, head_dim 128, bf16, seed 3,
 cut into 16 CP chunks of 8192 and run in Pass-KV ring order.  One step is one
-full pass: the 16 ring-step launches (all simulated ranks of a step in one
-launch) and the per-owner log-sum-exp merges.  Inputs are resident in HBM
-before timing starts.
+full ring: 16 ring-step launches (all simulated ranks' pairs of a step in one
+launch), each pair's partial (O, LSE) merged into its owner's running result
+in the launch's epilogue.  Inputs are resident in HBM before timing starts.
 
-The same JSON line also carries the dominant kernel's roofline (partial
-attention, measured with HIP events around each ring-step launch on the
-stream the library launches on), the split-KV decode leg (GB/s on the
-128 x 32768-key decode workload), the Pass-Q ordering of the prefill, the
-8K-token GQA workload (and, with --with-1m, the 1M-token one) as whole ring
-prefills, the merge kernel's bandwidth, and the fp64 CPU oracle timed on a
-bounded sample.
+The same JSON line carries the dominant kernel's roofline (HIP events around
+every ring-step launch, on the stream the library launches on), the Pass-Q
+ring, the ring with per-pair partials and a merge pass, the fused prefill, the
+8K-token GQA workload, 2048 new tokens against a 128K cached context (ring
+order chosen by exchanged bytes), the split-KV decode (with its
+allocation-free form), the KV-cache shard write and decode over the shards,
+the 1M-token workload, and the fp64 CPU oracle timed on a bounded sample.
 
-  python bench.py [--steps K] [--warmup W] [--gpus 1]
-  python bench.py --summarize-pmc FETCH_DIR WRITE_DIR [CLOCK_DIR [SQ_DIR [RDREQ_DIR]]]   # rocprofv3 --pmc summary
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-1m]
+  python bench.py --summarize-pmc FETCH_DIR WRITE_DIR [CLOCK_DIR [SQ_DIR [RDREQ_DIR]]]
+  python bench.py --summarize-trace TRACE_DIR BENCH_JSON
 """
 from __future__ import annotations
 
@@ -42,6 +43,8 @@ PREFILL = "prefill_bf16_s128k_p16"
 DECODE = "decode_b128_kv32k_p8"
 KERNEL_SRC = os.path.join(ROOT, "context_attention_cpattn_amd", "csrc", "partial_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "partial_bf16_prefill_s128k_p16_traffic.txt")
+TRACE_FILE = os.path.join(ROOT, "profiles", "partial_bf16_prefill_s128k_p16_trace.txt")
+PROFILE_CMD = "python bench.py --headline-only --no-cpu-baseline"
 COPY_BYTES = 1 << 30
 
 
@@ -74,13 +77,13 @@ def ring_step_flops(w, order: str):
     return out
 
 
-def pmc_values() -> dict:
-    """Numeric entries of the committed pmc summary; empty if it is absent or if a kernel source
-    changed since the counters were taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+def _summary_values(path: str, keep_text=()) -> dict:
+    """Entries of a committed profile summary (numbers, plus the text keys named); empty if the file
+    is absent or a kernel source changed since it was taken."""
+    if not os.path.exists(path):
         return {}
     kv = {}
-    for ln in open(TRAFFIC_FILE):
+    for ln in open(path):
         if ":" in ln and not ln.startswith("#"):
             a, b = ln.split(":", 1)
             kv[a.strip()] = b.strip()
@@ -88,11 +91,24 @@ def pmc_values() -> dict:
         return {}
     out = {}
     for key, val in kv.items():
+        if key in keep_text:
+            out[key] = val
+            continue
         try:
             out[key] = float(val.split()[0])
         except (ValueError, IndexError):
             pass
     return out
+
+
+def pmc_values() -> dict:
+    """Numeric entries of the committed counter summary of the current kernel sources."""
+    return _summary_values(TRAFFIC_FILE)
+
+
+def trace_values() -> dict:
+    """Entries of the committed kernel-trace summary of the current kernel sources."""
+    return _summary_values(TRACE_FILE, keep_text=("box_host", "box_gpu_uuid"))
 
 
 def read_pmc_summary():
@@ -103,28 +119,37 @@ def read_pmc_summary():
             kv.get("frac_of_peak_at_measured_sclk"))
 
 
+def cpu_threads() -> int:
+    """Host threads for the oracle: every core this process may run on, capped by OMP_NUM_THREADS
+    when it is set (the host's CPU share for this job)."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
 def cpu_baseline(w, q, k, v, seconds: float):
-    """fp64 oracle on sampled full-context rows of the prefill workload, on the host cores."""
+    """The fp64 oracle (``oracle.partial_attention``, as the parity tests call it) on blocks of 256
+    consecutive query rows at the end of the prefill workload, each against its full causal
+    context, for about ``seconds``: GEMM-shaped row blocks on the host cores."""
     import torch
 
     import oracle
-    import seeded_inputs as si
 
-    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    threads = cpu_threads()
     torch.set_num_threads(threads)
-    rows = si.sampled_rows(w, 1024)
-    rng = __import__("random").Random(0)
-    rows = rows[rng.sample(range(len(rows)), len(rows))]
-    k64, v64 = k.to(torch.float64), v.to(torch.float64)
-    done_flops, n = 0.0, 0
+    R = 256
+    S = w.Sq
+    done_flops, n_blocks = 0.0, 0
     t0 = time.perf_counter()
-    for pos in rows:
-        pos = int(pos)
-        oracle.attention_rows(q[:, pos:pos + 1], k64[:, :pos + 1], v64[:, :pos + 1], [pos], causal=True)
-        done_flops += 4.0 * w.D * w.Hq * w.B * (pos + 1)
-        n += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
+    while time.perf_counter() - t0 < seconds and (n_blocks + 1) * R <= S:
+        r1 = S - n_blocks * R
+        r0 = r1 - R
+        oracle.partial_attention(q[:, r0:r1], k[:, :r1], v[:, :r1], r0, 0, True, row_block=R)
+        # visible (query, key) pairs of rows r0..r1-1: sum of (pos + 1)
+        done_flops += 4.0 * w.D * w.Hq * w.B * (R * r0 + R * (R + 1) / 2)
+        n_blocks += 1
     dt = time.perf_counter() - t0
     cpu = "unknown"
     try:
@@ -132,10 +157,46 @@ def cpu_baseline(w, q, k, v, seconds: float):
             cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu)
     except OSError:
         pass
-    return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": torch.get_num_threads(), "kind": "oracle",
-            "cpu": cpu, "seconds": round(dt, 2),
-            "sample": f"{n} query rows x {w.Hq} heads of {w.name} at full causal context (fp64, torch CPU), "
-                      f"{done_flops:.3e} FLOP in {dt:.1f} s"}
+    return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "host_cpus_visible": len(os.sched_getaffinity(0)), "cpu": cpu, "seconds": round(dt, 2),
+            "sample": f"{n_blocks} blocks of {R} consecutive query rows (the last {n_blocks * R} rows) x {w.Hq} "
+                      f"heads of {w.name}, each row at its full causal context: oracle.partial_attention in fp64 "
+                      f"on torch CPU (GEMM-shaped row blocks), {done_flops:.3e} FLOP in {dt:.1f} s on {threads} "
+                      f"threads"}
+
+
+def box_id(torch) -> dict:
+    import socket
+    props = torch.cuda.get_device_properties(0)
+    uuid = str(getattr(props, "uuid", "")) or None
+    return {"host": socket.gethostname(), "gpu_uuid": uuid, "device": props.name}
+
+
+def timed_reps(torch, stream, fn, reps: int, warm_ms: float = 50.0):
+    """Median ms of ``reps`` calls of fn, each bracketed by events on ``stream``, after a warm-up of at
+    least two calls and ~warm_ms (the GPU sat idle while inputs were drawn on the host, and cold
+    calls run below the steady rate)."""
+    for _ in range(2):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    for _ in range(min(200, int(warm_ms / max(e0.elapsed_time(e1), 1e-3)))):
+        fn()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    for i in range(reps):
+        ev[i][0].record(stream)
+        fn()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return sorted(e[0].elapsed_time(e[1]) for e in ev)[reps // 2]
+
+
+def tf(flops: float, ms: float) -> dict:
+    t = flops / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 4), "TFLOP/s": round(t, 2), "pct_bf16_peak": round(100 * t / PEAK_BF16_TFLOPS, 2)}
 
 
 def main(argv=None) -> int:
@@ -143,26 +204,27 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--order", default="pass_kv", choices=["pass_kv", "pass_q"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--no-small", action="store_true", help="skip the 8K-token GQA workload leg")
-    ap.add_argument("--no-other-order", action="store_true",
-                    help="skip the other ring order (profiling runs: every partial launch is then a ring step)")
-    ap.add_argument("--with-1m", action="store_true",
-                    help="also time the 1M-token workload (about a minute more: inputs are 4 GiB of Q)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="only the timed Pass-KV ring steps (profiling runs: every partial-kernel launch is then a "
+                         "headline ring step)")
+    ap.add_argument("--no-1m", action="store_true", help="skip the 1M-token workload leg (~1 minute)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB fp32 copy kernel (counter calibration under rocprofv3 --pmc)")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
                     help="FETCH_DIR WRITE_DIR [CLOCK_DIR [SQ_DIR [RDREQ_DIR]]]: HBM traffic (shader clock, "
                          "MFMA busy fraction, read bytes by request size) from rocprofv3 --pmc runs")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"),
+                    help="kernel-trace summary of the headline kernel beside a plain bench line of the same box")
     args = ap.parse_args(argv)
 
     if args.summarize_pmc:
-        if len(args.summarize_pmc) not in (2, 3, 4, 5, 6):
-            ap.error("--summarize-pmc takes FETCH_DIR WRITE_DIR [CLOCK_DIR [SQ_DIR [RDREQ_DIR [TRACE_DIR]]]]")
+        if len(args.summarize_pmc) not in (2, 3, 4, 5):
+            ap.error("--summarize-pmc takes FETCH_DIR WRITE_DIR [CLOCK_DIR [SQ_DIR [RDREQ_DIR]]]")
         return summarize_pmc(*args.summarize_pmc)
+    if args.summarize_trace:
+        return summarize_trace(*args.summarize_trace)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
               "the simulated CP ranks all run on one device.", file=sys.stderr)
@@ -175,253 +237,243 @@ def main(argv=None) -> int:
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    props = torch.cuda.get_device_properties(dev)
+    box = box_id(torch)
     w = si.WORKLOADS[PREFILL]
-    log(f"[bench] {props.name}, {cp.version()}; drawing {w.name} inputs")
+    log(f"[bench] {box['device']} on {box['host']}, {cp.version()}; drawing {w.name} inputs")
     q, k, v = si.make_qkv(w)
     gq, gk, gv = q.to(dev), k.to(dev), v.to(dev)
     P = w.n_chunks
-    ws = torch.empty(cp.ring_prefill_workspace_size(gq, P, True), dtype=torch.uint8, device=dev)
     out = torch.empty(w.q_shape(), dtype=torch.float32, device=dev)
     lse = torch.empty(w.q_shape()[:3], dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream(dev)
-    step_flops = ring_step_flops(w, args.order)
+    stream = torch.cuda.current_stream(dev)  # the stream the library launches on
     total_flops = w.flops()
-    assert abs(sum(step_flops) - total_flops) / total_flops < 1e-9
 
-    def one_step(ev=None):
+    def ring_steps(order, ev=None):
+        """One Pass-KV (or Pass-Q) ring: P accumulating ring-step launches, each pair merged into its
+        owner's running (O, LSE) by the kernel that computes it."""
         for s in range(P):
             if ev is not None:
                 ev[s][0].record(stream)
-            cp.ring_step(gq, gk, gv, P, s, ws, args.order, True)
+            cp.ring_step_accumulate(gq, gk, gv, P, s, out, lse, order, True)
             if ev is not None:
                 ev[s][1].record(stream)
-        if ev is not None:
-            ev[P][0].record(stream)
-        cp.ring_merge(P, ws, out, lse, args.order, True)
-        if ev is not None:
-            ev[P][1].record(stream)
 
+    # ---- headline: the Pass-KV ring, one accumulating launch per ring step
+    step_flops = ring_step_flops(w, "pass_kv")
+    assert abs(sum(step_flops) - total_flops) / total_flops < 1e-9
     for _ in range(args.warmup):
-        one_step()
+        ring_steps("pass_kv")
     torch.cuda.synchronize()
-    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(P + 1)]
-              for _ in range(args.steps)]
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(P)] for _ in range(args.steps)]
     log(f"[bench] timing {args.steps} steps")
     t0 = time.perf_counter()
     for i in range(args.steps):
-        one_step(events[i])
+        ring_steps("pass_kv", events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall / args.steps * 1e3
     value = total_flops / (wall / args.steps) / 1e12
-
-    # dominant kernel: the partial-attention launches (one per ring step)
     k_ms = [[events[i][s][0].elapsed_time(events[i][s][1]) for s in range(P)] for i in range(args.steps)]
-    m_ms = [events[i][P][0].elapsed_time(events[i][P][1]) for i in range(args.steps)]
     kern_ms_total = sum(sum(x) for x in k_ms)
-    launches = args.steps * P
-    avg_launch_ms = kern_ms_total / launches
+    avg_launch_ms = kern_ms_total / (args.steps * P)
     achieved = total_flops * args.steps / (kern_ms_total * 1e-3) / 1e12
-    traffic, sclk, mfma_busy, frac_sclk = read_pmc_summary()
+    traffic, sclk, mfma_busy, _ = read_pmc_summary()
+    trace = trace_values()
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                # the chip does not hold 2.4 GHz under this kernel: the same fraction against the dense
-                # peak at the shader clock measured for it (rocprofv3 GRBM_GUI_ACTIVE, profiles/)
-                "sclk_ghz_measured": sclk,
-                "sclk_source": ("rocprofv3 GRBM_GUI_ACTIVE run of this kernel source, and the kernel trace "
-                                "taken beside it on the same box (profiles/partial_bf16_prefill_s128k_p16_traffic.txt); "
-                                "boxes differ by up to ~7%" if sclk else None),
-                "frac_at_measured_sclk": frac_sclk,
-                "mfma_busy_fraction_profiled": mfma_busy,
-                "kernel": "partial_bf16_d128_kernel", "launches_per_step": P,
-                "avg_launch_ms": round(avg_launch_ms, 4),
-                "algorithmic_flop_per_launch": total_flops / P}
+                "kernel": "partial_bf16_d128_kernel<false> (accumulating ring step)", "launches_per_step": P,
+                "avg_launch_ms": round(avg_launch_ms, 4), "algorithmic_flop_per_launch": total_flops / P,
+                "basis": "HIP events around every ring-step launch of the timed steps, on the stream the library "
+                         "launches on; this run's box",
+                "box": box}
+    if trace:
+        # the committed kernel trace of the same kernel source and launch pattern, with the box it ran on
+        roofline.update({"frac_profiled": trace.get("frac_profiled"),
+                         "avg_launch_ms_profiled": trace.get("partial_kernel_avg_ms"),
+                         "profiled_box": trace.get("box_host"),
+                         "profiled_source": "profiles/partial_bf16_prefill_s128k_p16_trace.txt"})
+    if sclk:
+        roofline.update({"sclk_ghz_profiled": sclk, "mfma_busy_fraction_profiled": mfma_busy,
+                         "counters_source": "profiles/partial_bf16_prefill_s128k_p16_traffic.txt"})
     per_step_tflops = [round(step_flops[s] / (sum(k_ms[i][s] for i in range(args.steps)) / args.steps * 1e-3) / 1e12, 1)
                        for s in range(P)]
-    # merge bandwidth: every owner reads its partials (O fp32 + LSE) and writes O fp32 + LSE
-    C, row_bytes = w.chunk, 4 * (w.D + 1)
-    n_parts = sum(i + 1 for i in range(P))
-    merge_bytes = (n_parts + P) * C * w.Hq * w.B * row_bytes
-    merge_ms = sum(m_ms) / len(m_ms)
-    log(f"[bench] step {ms_per_step:.2f} ms, {value:.1f} TFLOP/s; partial kernel {achieved:.1f} TFLOP/s; "
-        f"merge {merge_ms:.3f} ms")
-
+    log(f"[bench] step {ms_per_step:.2f} ms, {value:.1f} TFLOP/s; partial kernel {achieved:.1f} TFLOP/s per launch")
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": w.name, "order": args.order, "B": w.B, "S": w.Sq, "Hq": w.Hq, "Hkv": w.Hkv,
-                   "D": w.D, "n_chunks": P, "causal": True, "seed": w.seed, "inputs": "N(0,1) rounded to bf16",
-                   "flop_per_step": total_flops},
+        "config": {"workload": w.name, "order": "pass_kv", "launch": "16 accumulating ring-step launches "
+                   "(cpattn_ring_step_accumulate), the merge in each launch's epilogue", "B": w.B, "S": w.Sq,
+                   "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "n_chunks": P, "causal": True, "seed": w.seed,
+                   "inputs": "N(0,1) rounded to bf16", "flop_per_step": total_flops},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": roofline,
         "per_ring_step_tflops": per_step_tflops,
-        "merge": {"ms_per_step": round(merge_ms, 4), "GB/s": round(merge_bytes / (merge_ms * 1e-3) / 1e9, 1),
-                  "frac_hbm": round(merge_bytes / (merge_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                  "algorithmic_bytes": merge_bytes},
-        "device": props.name,
     }
+    if args.headline_only:
+        if args.calibrate_copy:
+            _copy_calibration(torch, dev)
+            result["copy_calibration_bytes"] = COPY_BYTES
+        print(json.dumps(result), flush=True)
+        return 0
 
-    # the other ring order of the same prefill, as whole ring prefills (all pairs in one launch)
-    if not args.no_other_order:
-        other = "pass_q" if args.order == "pass_kv" else "pass_kv"
-        ws2 = torch.empty(cp.ring_prefill_workspace_size(gq, P, True), dtype=torch.uint8, device=dev)
-        cp.ring_prefill(gq, gk, gv, P, other, True, out=out, lse=lse, workspace=ws2)
+    # ---- Pass-Q: the same ring with Q moving, one accumulating launch per ring step
+    ms_q = timed_reps(torch, stream, lambda: ring_steps("pass_q"), max(3, args.steps // 2))
+    result["pass_q"] = {**tf(total_flops, ms_q), "launch": "16 accumulating ring-step launches, Pass-Q schedule"}
+    log(f"[bench] pass_q {ms_q:.2f} ms")
+
+    # ---- the ring with per-pair partials in a workspace, then one merge launch (all owners)
+    ws = torch.empty(cp.ring_prefill_workspace_size(gq, P, True), dtype=torch.uint8, device=dev)
+    ev_m = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def ring_workspace(timed=False):
+        for s in range(P):
+            cp.ring_step(gq, gk, gv, P, s, ws, "pass_kv", True)
+        if timed:
+            ev_m[0].record(stream)
+        cp.ring_merge(P, ws, out, lse, "pass_kv", True)
+        if timed:
+            ev_m[1].record(stream)
+
+    ms_w = timed_reps(torch, stream, ring_workspace, max(3, args.steps // 2))
+    merge_ms = []
+    for _ in range(3):
+        ring_workspace(True)
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        reps = max(1, args.steps // 2)
-        for _ in range(reps):
-            cp.ring_prefill(gq, gk, gv, P, other, True, out=out, lse=lse, workspace=ws2)
-        torch.cuda.synchronize()
-        dt = (time.perf_counter() - t0) / reps
-        result[other] = {"ms_per_step": round(dt * 1e3, 3), "TFLOP/s": round(total_flops / dt / 1e12, 2),
-                         "launch": "ring_prefill: all pairs in one launch, then one merge"}
-        del ws2
+        merge_ms.append(ev_m[0].elapsed_time(ev_m[1]))
+    merge_ms = sorted(merge_ms)[1]
+    C, row_bytes = w.chunk, 4 * (w.D + 1)
+    n_parts = P * (P + 1) // 2
+    merge_bytes = (n_parts + P) * C * w.Hq * w.B * row_bytes
+    result["ring_workspace"] = {**tf(total_flops, ms_w), "launch": "16 ring_step launches into per-pair workspace "
+                                "slots, then one ring_merge launch",
+                                "merge": {"ms": round(merge_ms, 4), "GB/s": round(merge_bytes / (merge_ms * 1e-3) / 1e9, 1),
+                                          "frac_hbm": round(merge_bytes / (merge_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                          "algorithmic_bytes": merge_bytes}}
     del ws
+    log(f"[bench] ring with workspace {ms_w:.2f} ms (merge {merge_ms:.3f} ms)")
 
-    def fused_reps(xq, xk, xv, n_chunks: int, xout, xlse, reps: int, label: str):
-        """Median ms of whole fused ring prefills (online merge, one launch; 2 warm-ups)."""
-        for _ in range(2):
-            cp.ring_prefill_fused(xq, xk, xv, n_chunks, True, out=xout, lse=xlse)
-        torch.cuda.synchronize()
-        evf = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
-        for i in range(reps):
-            evf[i][0].record(stream)
-            cp.ring_prefill_fused(xq, xk, xv, n_chunks, True, out=xout, lse=xlse)
-            evf[i][1].record(stream)
-        torch.cuda.synchronize()
-        msf = sorted(e[0].elapsed_time(e[1]) for e in evf)[reps // 2]
-        log(f"[bench] {label} fused: {msf:.3f} ms")
-        return msf
+    # ---- fused: every owner walks its visible keys once, merge online, one launch
+    ms_f = timed_reps(torch, stream, lambda: cp.ring_prefill_fused(gq, gk, gv, P, True, out=out, lse=lse),
+                      max(3, args.steps // 2))
+    result["fused"] = {**tf(total_flops, ms_f), "launch": "ring_prefill_fused: one launch, each owner's visible "
+                       "keys in one pass, merge online"}
+    log(f"[bench] fused {ms_f:.2f} ms")
+    del gq, gk, gv, out, lse
+    torch.cuda.empty_cache()
 
-    # the same Pass-KV ring with each partial merged into the running (O, LSE) by the kernel that
-    # computes it: 16 launches per step, no workspace and no merge pass
-    if not args.no_other_order:
-        for _ in range(2):
-            for s_ in range(P):
-                cp.ring_step_accumulate(gq, gk, gv, P, s_, out, lse, args.order, True)
-        torch.cuda.synchronize()
-        reps_a = max(3, args.steps // 2)
-        ev_a = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps_a)]
-        for i in range(reps_a):
-            ev_a[i][0].record(stream)
-            for s_ in range(P):
-                cp.ring_step_accumulate(gq, gk, gv, P, s_, out, lse, args.order, True)
-            ev_a[i][1].record(stream)
-        torch.cuda.synchronize()
-        ms_a = sorted(e[0].elapsed_time(e[1]) for e in ev_a)[reps_a // 2]
-        tf_a = total_flops / (ms_a * 1e-3) / 1e12
-        log(f"[bench] {w.name} accumulating ring steps: {ms_a:.3f} ms, {tf_a:.1f} TFLOP/s")
-        result["accumulate"] = {"ms_per_step": round(ms_a, 3), "TFLOP/s": round(tf_a, 2),
-                                "pct_bf16_peak": round(100 * tf_a / PEAK_BF16_TFLOPS, 2),
-                                "launch": "ring_step_accumulate x 16: each partial merged into the running "
-                                          "result by the kernel that computes it, no merge pass"}
+    # ---- 8K-token GQA workload: whole ring prefills and the fused prefill
+    w8 = si.WORKLOADS["gqa16_bf16_s8k_p8"]
+    log(f"[bench] drawing {w8.name} inputs")
+    x = [t.to(dev) for t in si.make_qkv(w8)]
+    o8 = torch.empty(w8.q_shape(), dtype=torch.float32, device=dev)
+    l8 = torch.empty(w8.q_shape()[:3], dtype=torch.float32, device=dev)
+    ws8 = torch.empty(cp.ring_prefill_workspace_size(x[0], w8.n_chunks, True), dtype=torch.uint8, device=dev)
+    reps = max(10, args.steps)
+    ms8 = timed_reps(torch, stream, lambda: cp.ring_prefill(*x, w8.n_chunks, "pass_kv", True, out=o8, lse=l8,
+                                                               workspace=ws8), reps)
+    ms8f = timed_reps(torch, stream, lambda: cp.ring_prefill_fused(*x, w8.n_chunks, True, out=o8, lse=l8), reps)
+    result["gqa_8k"] = {"workload": w8.name, "order": "pass_kv", **tf(w8.flops(), ms8), "flop": w8.flops(),
+                        "launch": "ring_prefill: per-owner walk writing every pair's partial, then one merge",
+                        "fused": tf(w8.flops(), ms8f)}
+    log(f"[bench] 8K ring {ms8:.3f} ms, fused {ms8f:.3f} ms")
+    del x, o8, l8, ws8
 
-    if not args.no_other_order:
-        msf = fused_reps(gq, gk, gv, P, out, lse, max(3, args.steps // 2), w.name)
-        result["fused"] = {"ms_per_step": round(msf, 3), "TFLOP/s": round(total_flops / (msf * 1e-3) / 1e12, 2),
-                           "pct_bf16_peak": round(100 * total_flops / (msf * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
-                           "launch": "ring_prefill_fused: each owner's visible keys in one pass, no merge"}
+    # ---- 2048 new tokens against a 131072-token cached context: the order chosen by exchanged bytes
+    Sq, Skv = 2048, 131072 + 2048
+    qs = si.draw_tensor(811, si.TENSOR_Q, (1, Sq, 16, 128), torch.bfloat16).to(dev)
+    ks = si.draw_tensor(811, si.TENSOR_K, (1, Skv, 1, 128), torch.bfloat16).to(dev)
+    vs = si.draw_tensor(811, si.TENSOR_V, (1, Skv, 1, 128), torch.bfloat16).to(dev)
+    order, b_kv, b_q = cp.ring_select_order(qs, ks, 16, True)
+    f_s = 4.0 * 128 * 16 * sum(Skv - Sq + i + 1 for i in range(Sq))
+    os_ = torch.empty(1, Sq, 16, 128, dtype=torch.float32, device=dev)
+    ls_ = torch.empty(1, Sq, 16, dtype=torch.float32, device=dev)
+    ms_s = timed_reps(torch, stream, lambda: cp.ring_prefill(qs, ks, vs, 16, "auto", True, out=os_, lse=ls_), reps)
+    ms_sf = timed_reps(torch, stream, lambda: cp.ring_prefill_fused(qs, ks, vs, 16, True, out=os_, lse=ls_), reps)
+    result["suffix_2048_on_128k"] = {"workload": "2048 new tokens x 16/1 heads, D=128, against 131072 cached "
+                                     "tokens, 16 chunks, bf16, seed 811", "order_selected": order,
+                                     "exchanged_bytes": {"pass_kv": b_kv, "pass_q": b_q}, "flop": f_s,
+                                     **tf(f_s, ms_s), "fused": tf(f_s, ms_sf)}
+    log(f"[bench] 2048 on 128K ({order}) {ms_s:.3f} ms, fused {ms_sf:.3f} ms")
+    del qs, ks, vs, os_, ls_
 
-    def prefill_leg(name: str, reps: int):
-        """Median time of whole Pass-KV ring prefills of another workload, timed back to back after
-        a warm-up of at least two calls and ~50 ms (the GPU idled while the inputs were drawn)."""
-        wx = si.WORKLOADS[name]
-        log(f"[bench] drawing {wx.name} inputs")
-        xq_, xk_, xv_ = si.make_qkv(wx)
-        xq, xk, xv = xq_.to(dev), xk_.to(dev), xv_.to(dev)
-        del xq_, xk_, xv_
-        xws = torch.empty(cp.ring_prefill_workspace_size(xq, wx.n_chunks, True), dtype=torch.uint8,
-                          device=dev)
-        xout = torch.empty(wx.q_shape(), dtype=torch.float32, device=dev)
-        xlse = torch.empty(wx.q_shape()[:3], dtype=torch.float32, device=dev)
-        def run():
-            cp.ring_prefill(xq, xk, xv, wx.n_chunks, "pass_kv", True, out=xout, lse=xlse, workspace=xws)
+    # ---- split-KV decode, its allocation-free form, decode over CP cache shards, and the cache write
+    wd = si.WORKLOADS[DECODE]
+    log(f"[bench] drawing {wd.name} inputs")
+    dq, dk, dv = [t.to(dev) for t in si.make_qkv(wd)]
+    dws = torch.empty(cp.splitkv_decode_workspace_size(dq, dk, wd.n_chunks), dtype=torch.uint8, device=dev)
+    dout = torch.empty(wd.q_shape(), dtype=torch.float32, device=dev)
+    dlse = torch.empty(wd.q_shape()[:3], dtype=torch.float32, device=dev)
+    dreps = max(20, args.steps)
+    ms_d = timed_reps(torch, stream, lambda: cp.splitkv_decode(dq, dk, dv, wd.n_chunks, out=dout, lse=dlse,
+                                                               workspace=dws), dreps, warm_ms=60.0)
+    ms_dn = timed_reps(torch, stream, lambda: cp.splitkv_decode_noalloc(dq, dk, dv, wd.n_chunks, dout, dlse), dreps)
+    kv_bytes = 2 * wd.B * wd.Skv * wd.Hkv * wd.D * 2
+    q_bytes = wd.B * wd.Hq * wd.D * 2
+    part_bytes = wd.n_chunks * wd.B * wd.Hq * (wd.D + 1) * 4
+    out_bytes = wd.B * wd.Hq * (wd.D + 1) * 4
+    dec_bytes = kv_bytes + q_bytes + 2 * part_bytes + out_bytes
 
-        for _ in range(2):
-            run()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        run()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        for _ in range(min(200, int(50.0 / max(e0.elapsed_time(e1), 1e-3)))):
-            run()
-        evx = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
-        for i in range(reps):
-            evx[i][0].record(stream)
-            run()
-            evx[i][1].record(stream)
-            if wx.flops() > 1e15:  # long calls: report progress as they finish
+    def gbs(nbytes, ms):
+        g = nbytes / (ms * 1e-3) / 1e9
+        return {"ms": round(ms, 4), "GB/s": round(g, 1), "frac_hbm": round(g / PEAK_HBM_GBS, 4)}
+
+    result["decode"] = {"workload": wd.name, **gbs(dec_bytes, ms_d), "algorithmic_bytes": dec_bytes,
+                        "peak_GB/s": PEAK_HBM_GBS, "noalloc": gbs(dec_bytes, ms_dn)}
+    pmc = pmc_values()
+    if "decode_fetch_bytes_per_launch" in pmc and "decode_write_bytes_per_launch" in pmc:
+        result["decode"]["kernel_traffic_profiled"] = pmc["decode_fetch_bytes_per_launch"] + \
+            pmc["decode_write_bytes_per_launch"]
+    log(f"[bench] decode {ms_d:.3f} ms, no-alloc {ms_dn:.3f} ms")
+    # the same cache as the KV shards of 8 CP ranks, each with room for 64 more tokens
+    C = wd.Skv // wd.n_chunks
+    ks8 = [torch.empty(wd.B, C + 64, wd.Hkv, wd.D, dtype=torch.bfloat16, device=dev) for _ in range(wd.n_chunks)]
+    vs8 = [torch.empty_like(t) for t in ks8]
+    ms_w8 = timed_reps(torch, stream, lambda: cp.kv_cache_write(dk, dv, wd.n_chunks, ks8, vs8), dreps)
+    lens = [C] * wd.n_chunks
+    cws = torch.empty(cp.cp_decode_workspace_size(dq, ks8), dtype=torch.uint8, device=dev)
+    ms_cd = timed_reps(torch, stream, lambda: cp.cp_decode(dq, ks8, vs8, lens, out=dout, lse=dlse, workspace=cws),
+                       dreps)
+    result["cache_write"] = {"what": f"{wd.name} K/V written into {wd.n_chunks} shards of {C + 64} rows",
+                             **gbs(2 * kv_bytes, ms_w8), "algorithmic_bytes": 2 * kv_bytes}
+    result["cp_decode"] = {"what": f"{wd.name} new tokens against the {wd.n_chunks} shards",
+                           **gbs(dec_bytes, ms_cd), "algorithmic_bytes": dec_bytes}
+    log(f"[bench] cache write {ms_w8:.3f} ms, decode over shards {ms_cd:.3f} ms")
+    del dq, dk, dv, dws, dout, dlse, ks8, vs8, cws
+    torch.cuda.empty_cache()
+
+    # ---- the 1M-token workload (Pass-KV ring with per-pair partials and merge, and the fused walk)
+    if not args.no_1m:
+        w1 = si.WORKLOADS["prefill_bf16_s1m_p8"]
+        log(f"[bench] drawing {w1.name} inputs")
+        x = [t.to(dev) for t in si.make_qkv(w1)]
+        o1 = torch.empty(w1.q_shape(), dtype=torch.float32, device=dev)
+        l1 = torch.empty(w1.q_shape()[:3], dtype=torch.float32, device=dev)
+        ws1 = torch.empty(cp.ring_prefill_workspace_size(x[0], w1.n_chunks, True), dtype=torch.uint8, device=dev)
+        res1 = {}
+        for name, fn in (("ring_prefill", lambda: cp.ring_prefill(*x, w1.n_chunks, "pass_kv", True, out=o1, lse=l1,
+                                                                  workspace=ws1)),
+                         ("fused", lambda: cp.ring_prefill_fused(*x, w1.n_chunks, True, out=o1, lse=l1))):
+            fn()
+            torch.cuda.synchronize()
+            ts = []
+            for i in range(3):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
                 torch.cuda.synchronize()
-                log(f"[bench] {wx.name} rep {i + 1}/{reps}: {evx[i][0].elapsed_time(evx[i][1]):.3f} ms")
-        torch.cuda.synchronize()
-        msx = sorted(e[0].elapsed_time(e[1]) for e in evx)[reps // 2]
-        tf = wx.flops() / (msx * 1e-3) / 1e12
-        del xws
-        msf = fused_reps(xq, xk, xv, wx.n_chunks, xout, xlse, reps, wx.name)
-        tff = wx.flops() / (msf * 1e-3) / 1e12
-        del xq, xk, xv, xout, xlse
+                ts.append(e0.elapsed_time(e1))
+                log(f"[bench] {w1.name} {name} rep {i + 1}/3: {ts[-1]:.1f} ms")
+            res1[name] = tf(w1.flops(), sorted(ts)[1])
+        result["prefill_1m"] = {"workload": w1.name, "order": "pass_kv", "flop": w1.flops(), **res1["ring_prefill"],
+                                "launch": "ring_prefill: all pairs in one launch, then one merge",
+                                "fused": res1["fused"]}
+        del x, o1, l1, ws1
         torch.cuda.empty_cache()
-        return {"workload": wx.name, "order": "pass_kv", "ms": round(msx, 4), "TFLOP/s": round(tf, 2),
-                "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2), "flop": wx.flops(), "reps": reps,
-                "fused": {"ms": round(msf, 4), "TFLOP/s": round(tff, 2),
-                          "pct_bf16_peak": round(100 * tff / PEAK_BF16_TFLOPS, 2)}}
-
-    if not args.no_small:
-        result["gqa_8k"] = prefill_leg("gqa16_bf16_s8k_p8", max(5, args.steps))
-
-    if not args.no_decode:
-        wd = si.WORKLOADS[DECODE]
-        log(f"[bench] drawing {wd.name} inputs")
-        dq_, dk_, dv_ = si.make_qkv(wd)
-        dq, dk, dv = dq_.to(dev), dk_.to(dev), dv_.to(dev)
-        del dq_, dk_, dv_
-        dws = torch.empty(cp.splitkv_decode_workspace_size(dq, dk, wd.n_chunks), dtype=torch.uint8, device=dev)
-        dout = torch.empty(wd.q_shape(), dtype=torch.float32, device=dev)
-        dlse = torch.empty(wd.q_shape()[:3], dtype=torch.float32, device=dev)
-        # ~60 ms of decodes first: the inputs were drawn on the host meanwhile the GPU sat idle, and
-        # the first calls after an idle spell run below the steady rate (measured: 0.40 ms median
-        # cold against 0.37 ms after a busy spell, the same 0.36 ms minimum)
-        for _ in range(160):
-            cp.splitkv_decode(dq, dk, dv, wd.n_chunks, out=dout, lse=dlse, workspace=dws)
-        torch.cuda.synchronize()
-        reps = max(20, args.steps)
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
-        for i in range(reps):
-            ev[i][0].record(stream)
-            cp.splitkv_decode(dq, dk, dv, wd.n_chunks, out=dout, lse=dlse, workspace=dws)
-            ev[i][1].record(stream)
-        torch.cuda.synchronize()
-        ms = sorted(e[0].elapsed_time(e[1]) for e in ev)[reps // 2]
-        kv_bytes = 2 * wd.B * wd.Skv * wd.Hkv * wd.D * 2
-        q_bytes = wd.B * wd.Hq * wd.D * 2
-        part_bytes = wd.n_chunks * wd.B * wd.Hq * (wd.D + 1) * 4
-        out_bytes = wd.B * wd.Hq * (wd.D + 1) * 4
-        dec_bytes = kv_bytes + q_bytes + 2 * part_bytes + out_bytes
-        gbs = dec_bytes / (ms * 1e-3) / 1e9
-        result["decode"] = {"workload": wd.name, "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
-                            "ms": round(ms, 4), "algorithmic_bytes": dec_bytes, "peak_GB/s": PEAK_HBM_GBS}
-        pmc = pmc_values()
-        if "decode_fetch_bytes_per_launch" in pmc and "decode_write_bytes_per_launch" in pmc:
-            # HBM bytes the decode kernel itself moved per call (counters, copy-calibrated; the
-            # 8-way merge after it is not included), from the committed summary of this source
-            result["decode"]["kernel_traffic_profiled"] = pmc["decode_fetch_bytes_per_launch"] + \
-                pmc["decode_write_bytes_per_launch"]
-        log(f"[bench] decode {ms:.3f} ms, {gbs:.0f} GB/s")
-        del dq, dk, dv, dws
-
-    # the optional 1M-token leg runs last: it keeps the chip at full MFMA load for about 20 s
-    if args.with_1m:
-        result["prefill_1m"] = prefill_leg("prefill_bf16_s1m_p8", 3)
 
     if args.calibrate_copy:
-        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
+        _copy_calibration(torch, dev)
         result["copy_calibration_bytes"] = COPY_BYTES
 
     if not args.no_cpu_baseline:
@@ -429,6 +481,14 @@ def main(argv=None) -> int:
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def _copy_calibration(torch, dev) -> None:
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
 
 
 def _prefill_workload():
@@ -475,7 +535,7 @@ def _read_bytes_by_size(rows, name_part: str):
 
 
 def summarize_pmc(fetch_dir: str, write_dir: str, clock_dir: str | None = None, sq_dir: str | None = None,
-                  rdreq_dir: str | None = None, trace_dir: str | None = None) -> int:
+                  rdreq_dir: str | None = None) -> int:
     """HBM bytes per partial-kernel launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
     each scaled by what the same counter reads for the 1 GiB copy kernel; with a third run of
     GRBM_GUI_ACTIVE, also the shader clock the partial kernel ran at; with a fourth run of
@@ -496,9 +556,9 @@ def summarize_pmc(fetch_dir: str, write_dir: str, clock_dir: str | None = None, 
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         f.write("# HBM traffic of partial_bf16_d128_kernel per launch on the 128K-token workload, Pass-KV\n")
-        f.write("# from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs of:\n")
-        f.write("#   python bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-small --no-other-order --calibrate-copy\n")
-        f.write("# (every partial launch of that run is one Pass-KV ring step; the decode leg runs after it)\n")
+        f.write("# accumulating ring steps, from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs of:\n")
+        f.write(f"#   {PROFILE_CMD} --steps 1 --warmup 0 --calibrate-copy\n")
+        f.write("# (every partial launch of that run is one Pass-KV ring step)\n")
         f.write("# each counter scaled by its reading for a plain 1 GiB fp32 copy kernel\n")
         f.write(f"kernel_source_sha256_16: {kernel_hash()}\n")
         f.write(f"dispatches: {nf} (FETCH) {nw} (WRITE)\n")
@@ -537,24 +597,6 @@ def summarize_pmc(fetch_dir: str, write_dir: str, clock_dir: str | None = None, 
             f.write("# shader clock from a third run with --pmc GRBM_GUI_ACTIVE: busy clocks / 8 XCDs / dispatch time\n")
             f.write(f"sclk_ghz_partial_kernel: {ck:.3f}\n")
             f.write(f"sclk_ghz_copy_kernel: {cc:.3f}\n")
-            if trace_dir:
-                # the kernel trace of the same box: its average partial-kernel launch against the dense
-                # peak at the clock above (both from this box, unlike a live bench run elsewhere)
-                stats = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
-                avg_ns = None
-                for path in stats:
-                    with open(path, newline="") as sf:
-                        for r in csv.DictReader(sf):
-                            if "partial_bf16_d128_kernel" in r.get("Name", ""):
-                                avg_ns = float(r["AverageNs"])
-                if avg_ns:
-                    w = _prefill_workload()
-                    tf = w.flops() / w.n_chunks / (avg_ns * 1e-9) / 1e12
-                    f.write("# the kernel trace of the same box: average partial-kernel launch, its rate, and that\n"
-                            "# rate against the dense bf16 peak scaled to the clock above\n")
-                    f.write(f"trace_avg_ms_partial_kernel: {avg_ns / 1e6:.4f}\n")
-                    f.write(f"trace_tflops_partial_kernel: {tf:.1f}\n")
-                    f.write(f"frac_of_peak_at_measured_sclk: {tf / (PEAK_BF16_TFLOPS * ck / 2.4):.4f}\n")
         if sq_dir:
             sr = _pmc_rows(sq_dir)
             k = "partial_bf16_d128_kernel"
@@ -576,6 +618,54 @@ def summarize_pmc(fetch_dir: str, write_dir: str, clock_dir: str | None = None, 
             f.write(f"lds_bank_conflict_cycles_per_lds_active_cycle: "
                     f"{tot['SQ_LDS_BANK_CONFLICT'] / tot['SQ_LDS_IDX_ACTIVE']:.3f}\n")
     print(open(TRAFFIC_FILE).read())
+    return 0
+
+
+def summarize_trace(trace_dir: str, bench_json: str) -> int:
+    """Kernel-trace summary of the headline kernel (``rocprofv3 --kernel-trace --stats`` of the
+    headline-only bench) next to the plain bench line taken in the same call on the same box."""
+    w = _prefill_workload()
+    stats = {}
+    for path in glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True):
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                stats[r["Name"]] = (int(r["Calls"]), float(r["AverageNs"]), float(r["TotalDurationNs"]))
+    part = [(n, v) for n, v in stats.items() if "partial_bf16_d128_kernel" in n]
+    if not part:
+        raise SystemExit(f"no partial_bf16_d128_kernel dispatches in {trace_dir}")
+    calls = sum(v[0] for _, v in part)
+    avg_ns = sum(v[2] for _, v in part) / calls
+    line = json.loads([ln for ln in open(bench_json) if ln.strip().startswith("{")][-1])
+    rl = line["roofline"]
+    flop_launch = w.flops() / w.n_chunks
+    tfl = flop_launch / (avg_ns * 1e-9) / 1e12
+    os.makedirs(os.path.dirname(TRACE_FILE), exist_ok=True)
+    with open(TRACE_FILE, "w") as f:
+        f.write("# Kernel trace of the headline: 128K-token Pass-KV ring, 16 accumulating ring-step launches per step.\n")
+        f.write("# On the MI355X box, from /tmp with TMPDIR=/tmp, R = repository root:\n")
+        f.write(f"#   rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/trace -o kt -- "
+                f"{PROFILE_CMD} --steps 5 --warmup 1\n")
+        f.write(f"#   python bench.py --summarize-trace gpurun_out/trace gpurun_out/bench_plain.json\n")
+        f.write("# where gpurun_out/bench_plain.json is the plain `python bench.py` line of the same call (same box).\n")
+        f.write(f"kernel_source_sha256_16: {kernel_hash()}\n")
+        f.write(f"box_host: {line['roofline'].get('box', {}).get('host')}\n")
+        f.write(f"box_gpu_uuid: {line['roofline'].get('box', {}).get('gpu_uuid')}\n")
+        f.write(f"partial_kernel_dispatches: {calls}\n")
+        f.write(f"partial_kernel_avg_ms: {avg_ns / 1e6:.4f}\n")
+        f.write(f"flop_per_launch: {flop_launch:.6e}\n")
+        f.write(f"tflops_profiled: {tfl:.1f}\n")
+        f.write(f"frac_profiled: {tfl / PEAK_BF16_TFLOPS:.4f}\n")
+        f.write(f"trace_kernel_ms_per_step: {avg_ns * w.n_chunks / 1e6:.3f}\n")
+        f.write("# the plain bench line of the same call (HIP events around each launch; no profiler attached)\n")
+        f.write(f"bench_ms_per_step: {line['ms_per_step']}\n")
+        f.write(f"bench_value_tflops: {line['value']}\n")
+        f.write(f"bench_avg_launch_ms: {rl['avg_launch_ms']}\n")
+        f.write(f"bench_frac: {rl['frac']}\n")
+        f.write("# every kernel of the traced run: calls, average ms\n")
+        for n, (c, a_ns, _) in sorted(stats.items(), key=lambda kv_: -kv_[1][2]):
+            short = n.split("(")[0][:90]
+            f.write(f"kernel {short}: {c} {a_ns / 1e6:.4f}\n")
+    print(open(TRACE_FILE).read())
     return 0
 
 

@@ -66,3 +66,41 @@ def test_counter_summary_scales_by_the_copy_kernel(tmp_path, monkeypatch):
     assert hbm == pytest.approx(2000.0 * 2048 + 500.0 * 1024) and clk == pytest.approx(1.6)
     out.write_text(out.read_text().replace(bench.kernel_hash(), "0" * 16))
     assert bench.read_pmc_summary() == (None, None, None, None)
+
+
+def test_trace_summary_and_its_readback(tmp_path, monkeypatch):
+    """The kernel-trace summary: average partial-kernel launch -> TFLOP/s and fraction of the dense
+    peak, beside the plain bench line of the same box; read back only for the same kernel sources."""
+    import json
+    out = tmp_path / "trace.txt"
+    monkeypatch.setattr(bench, "TRACE_FILE", str(out))
+    d = tmp_path / "tr"
+    d.mkdir()
+    with open(d / "kt_kernel_stats.csv", "w", newline="") as f:
+        wr = csv.writer(f)
+        wr.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"])
+        wr.writerow(["partial_bf16_d128_kernel<false>(args)", 96, 96 * 3.5e6, 3.5e6, 99.0, 1e6, 7e6, 1.0])
+        wr.writerow(["decode_stream_kernel<128>(args)", 10, 3.3e6, 3.3e5, 1.0, 3e5, 4e5, 1.0])
+    bj = tmp_path / "b.json"
+    bj.write_text(json.dumps({"ms_per_step": 57.0, "value": 1234.5,
+                              "roofline": {"avg_launch_ms": 3.45, "frac": 0.51, "box": {"host": "boxA", "gpu_uuid": "u"}}}))
+    assert bench.summarize_trace(str(d), str(bj)) == 0
+    w = si.WORKLOADS["prefill_bf16_s128k_p16"]
+    tv = bench.trace_values()
+    assert tv["box_host"] == "boxA"
+    assert tv["partial_kernel_avg_ms"] == pytest.approx(3.5)
+    assert tv["frac_profiled"] == pytest.approx(w.flops() / 16 / 3.5e-3 / 1e12 / bench.PEAK_BF16_TFLOPS, abs=1e-4)
+    assert tv["trace_kernel_ms_per_step"] == pytest.approx(56.0)
+    assert tv["bench_ms_per_step"] == pytest.approx(57.0)
+    out.write_text(out.read_text().replace(bench.kernel_hash(), "0" * 16))
+    assert bench.trace_values() == {}
+
+
+def test_cpu_threads_respect_the_job_share(monkeypatch):
+    n = len(os.sched_getaffinity(0))
+    monkeypatch.setenv("OMP_NUM_THREADS", "1")
+    assert bench.cpu_threads() == 1
+    monkeypatch.setenv("OMP_NUM_THREADS", str(10 * n))
+    assert bench.cpu_threads() == n
+    monkeypatch.delenv("OMP_NUM_THREADS")
+    assert bench.cpu_threads() == n
