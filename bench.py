@@ -656,6 +656,8 @@ def summarize_trace(trace_dir: str, bench_json: str) -> int:
         f.write(f"tflops_profiled: {tfl:.1f}\n")
         f.write(f"frac_profiled: {tfl / PEAK_BF16_TFLOPS:.4f}\n")
         f.write(f"trace_kernel_ms_per_step: {avg_ns * w.n_chunks / 1e6:.3f}\n")
+        f.write("# (the traced run has the profiler attached and runs after the plain bench; its launches\n"
+                "# read a little longer than the plain run's event timing)\n")
         f.write("# the plain bench line of the same call (HIP events around each launch; no profiler attached)\n")
         f.write(f"bench_ms_per_step: {line['ms_per_step']}\n")
         f.write(f"bench_value_tflops: {line['value']}\n")
@@ -663,7 +665,7 @@ def summarize_trace(trace_dir: str, bench_json: str) -> int:
         f.write(f"bench_frac: {rl['frac']}\n")
         f.write("# every kernel of the traced run: calls, average ms\n")
         for n, (c, a_ns, _) in sorted(stats.items(), key=lambda kv_: -kv_[1][2]):
-            short = n.split("(")[0][:90]
+            short = n.replace("void ", "").replace("(anonymous namespace)::", "").split("(")[0][:90]
             f.write(f"kernel {short}: {c} {a_ns / 1e6:.4f}\n")
     print(open(TRACE_FILE).read())
     return 0
