@@ -5,10 +5,12 @@ the bench.  It holds the workload shapes and the random draws only: no step of
 the attention method (no scores, softmax, masking or merging) lives here, so the
 oracle and the HIP path stay independent while consuming identical inputs.
 
-Distribution and seeds follow the workloads the CP attention pages imply
-(Meta's "Scaling LLM Inference" article, section "Context Parallelism for
-Million-Token Contexts"): Q, K and V entries i.i.d. N(0, 1), one seed per
-workload, rounded to bf16 (round to nearest even) except the fp32 tiny case.
+The pages on context parallelism say nothing about inputs: they report
+whole-model prefills that need trained weights.  These synthetic workloads stand
+in for them at one GPU's share of such a layer, with shapes, chunk counts,
+dtypes and seeds fixed in the workload table below: Q, K and V entries i.i.d.
+N(0, 1), one seed per workload, rounded to bf16 (round to nearest even) except
+the fp32 tiny case.
 
 Stream definition (so that any machine reproduces the same tensors):
 each tensor is flattened in [B, S, H, D] order and cut into chunks of
