@@ -130,7 +130,7 @@ def pin_bytes_equal_length_closed_form(bytes_fn):
                 qb = P * (P - 1) * B * C * Hq * D * e + remote * B * C * Hq * (D + 1) * 4
                 assert bytes_fn(P, PASS_KV, causal, B, P * C, P * C, Hq, Hkv, D, e) == kv
                 assert bytes_fn(P, PASS_Q, causal, B, P * C, P * C, Hq, Hkv, D, e) == qb
-                # at equal lengths Pass-KV never moves more
+                # at equal lengths with 2-byte elements Pass-KV never moves more
                 assert _pick(bytes_fn, P, causal, B, P * C, P * C, Hq, Hkv, D, e) == PASS_KV
 
 
