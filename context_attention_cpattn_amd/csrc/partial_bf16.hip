@@ -597,165 +597,175 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
     for (int i = 0; i < NST - 1; ++i)
       if (i < n_tiles) fetch(i);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    {
-      // Q fragments, B operand of S^T = K Q^T: column = this lane's row,
-      // k-slots = d in [16 s + 8 g, 16 s + 8 g + 8)
-      const int rr = wave * 32 + l32;
-      const bool ok = row < a.Sq;
-#pragma unroll
-      for (int s2 = 0; s2 < NDS; ++s2)
-        qf[s2] = ok ? as_bf16x8(ld_lds16(qsm + rr * 256 + (((2 * s2 + g) ^ (rr & 15)) << 4))) : (bf16x8){};
-    }
-    {
-      scores(smem, snA);
-      mask_tile(snA, 0);
-      move_to_max(snA);
-      need = false;  // O is still zero
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const float p0 = prob(snA[0][2 * w]);
-        const float p1 = prob(snA[0][2 * w + 1]);
-        pwA[w] = pack_bf16(p0, p1);
+    if (r0 >= a.Sq) {
+      // No row of this wave is a query (a block shorter than the workgroup's
+      // 256 rows): keep the others' fetch and barrier schedule, skip the math,
+      // so the SIMD's matrix core serves the other wave alone.
+      for (int t = 0; t < n_tiles; ++t) {
+        if (t + NST - 1 < n_tiles) fetch((t + NST - 1) % NST);
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
       }
-    }
-
-    // Iteration t.  The last one also computes scores for the tile after the
-    // last: every one of them is masked (that tile starts at or past the
-    // block's last visible key), so its probabilities are 0; its K operands
-    // come from a stale stage that no fetch is writing.
-    auto iteration = [&](int t, auto st_tag, f32x16 (&sn)[2], f32x16 (&x)[2], uint32_t (&pw)[16],
-                         uint32_t (&pn)[16]) {
-      constexpr int ST = decltype(st_tag)::value;
-      constexpr int SN = (ST + 1) % NST;
-      constexpr int SL = (ST + NST - 1) % NST;
-      const uint8_t* cur = smem + ST * TBYTES;  // K of tile t at cur, V at cur + VBASE (voff)
-      const uint8_t* nxt = smem + SN * TBYTES;
-      // tile t+2 goes into the stage tile t-1 used
-      const bool do_fetch = t + NST - 1 < n_tiles;
-      if (do_fetch) fetch(SL);
-
-      u32x4 kop[16];
-      u32x2 vlo[16], vhi[16];
-      auto read_v = [&](int jj) {  // operands of PV MFMA jj: u = jj >> 2, db = jj & 3
-        const int u = jj >> 2, db = jj & 3;
-        vlo[jj] = ld_lds8_tr(cur + voff[db] + (16 * u) * 256);
-        vhi[jj] = ld_lds8_tr(cur + voff[db] + (16 * u + 8) * 256);
-      };
-      // ---- phase A: S(t+1) = K(t+1) Q^T; key block 1 of P(t) ----
-      __builtin_amdgcn_s_setprio(1);
-      const f32x16& s1 = sn[1];
-      x[0] = (f32x16){};
-      x[1] = (f32x16){};
+    } else {
+      {
+        // Q fragments, B operand of S^T = K Q^T: column = this lane's row,
+        // k-slots = d in [16 s + 8 g, 16 s + 8 g + 8)
+        const int rr = wave * 32 + l32;
+        const bool ok = row < a.Sq;
 #pragma unroll
-      for (int j = 0; j < KLA; ++j) kop[j] = ld_lds16(nxt + koff[j >> 1] + (j & 1) * 8192);
-      float pe = 0.f, pp = 0.f;
-      float xa = fmaf(s1[0], SCALE_LOG2, -mref);
-      pin(xa);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int s2 = 0; s2 < NDS; ++s2)
+          qf[s2] = ok ? as_bf16x8(ld_lds16(qsm + rr * 256 + (((2 * s2 + g) ^ (rr & 15)) << 4))) : (bf16x8){};
+      }
+      {
+        scores(smem, snA);
+        mask_tile(snA, 0);
+        move_to_max(snA);
+        need = false;  // O is still zero
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        if (j + KLA < 16) kop[j + KLA] = ld_lds16(nxt + koff[(j + KLA) >> 1] + ((j + KLA) & 1) * 8192);
-        if (j >= 16 - VLA) read_v(j - (16 - VLA));
-        x[j & 1] = mfma32(as_bf16x8(kop[j]), qf[j >> 1], x[j & 1]);
-        // slot j: exponent of score j, argument of score j+1, sum and pack of score j-1
-        const float pv = fast_exp2(xa);
-        if (j < 15) xa = fmaf(s1[j + 1], SCALE_LOG2, -mref);
-        if (j > 0) {
-          lt += pp;
-          if ((j - 1) & 1) {
-            pw[8 + ((j - 1) >> 1)] = pack_bf16(pe, pp);
-            pin(pw[8 + ((j - 1) >> 1)]);
-          } else {
-            pe = pp;
-            pin(pe);
-          }
+        for (int w = 0; w < 8; ++w) {
+          const float p0 = prob(snA[0][2 * w]);
+          const float p1 = prob(snA[0][2 * w + 1]);
+          pwA[w] = pack_bf16(p0, p1);
         }
-        pp = pv;
-        pin(pp);
-        pin(xa);
-        pin(lt);
-        __builtin_amdgcn_sched_barrier(0);
       }
-      lt += pp;
-      pw[15] = pack_bf16(pe, pp);
-      mask_tile(x, t + 1);
-      // tile t is complete: keep it, or take the slow path
-      if (__any(!(lt <= kTwoTau) || m == kNegInf)) redo_tile(cur, t, pw);
-      l += lt;
-      lt = 0.f;
-      __builtin_amdgcn_sched_barrier(0);
 
-      // ---- phase B: O^T += V(t)^T P(t)^T; key block 0 of P(t+1) ----
-      __builtin_amdgcn_s_setprio(0);
-      if (need) {
+      // Iteration t.  The last one also computes scores for the tile after the
+      // last: every one of them is masked (that tile starts at or past the
+      // block's last visible key), so its probabilities are 0; its K operands
+      // come from a stale stage that no fetch is writing.
+      auto iteration = [&](int t, auto st_tag, f32x16 (&sn)[2], f32x16 (&x)[2], uint32_t (&pw)[16],
+                           uint32_t (&pn)[16]) {
+        constexpr int ST = decltype(st_tag)::value;
+        constexpr int SN = (ST + 1) % NST;
+        constexpr int SL = (ST + NST - 1) % NST;
+        const uint8_t* cur = smem + ST * TBYTES;  // K of tile t at cur, V at cur + VBASE (voff)
+        const uint8_t* nxt = smem + SN * TBYTES;
+        // tile t+2 goes into the stage tile t-1 used
+        const bool do_fetch = t + NST - 1 < n_tiles;
+        if (do_fetch) fetch(SL);
+
+        u32x4 kop[16];
+        u32x2 vlo[16], vhi[16];
+        auto read_v = [&](int jj) {  // operands of PV MFMA jj: u = jj >> 2, db = jj & 3
+          const int u = jj >> 2, db = jj & 3;
+          vlo[jj] = ld_lds8_tr(cur + voff[db] + (16 * u) * 256);
+          vhi[jj] = ld_lds8_tr(cur + voff[db] + (16 * u + 8) * 256);
+        };
+        // ---- phase A: S(t+1) = K(t+1) Q^T; key block 1 of P(t) ----
+        __builtin_amdgcn_s_setprio(1);
+        const f32x16& s1 = sn[1];
+        x[0] = (f32x16){};
+        x[1] = (f32x16){};
 #pragma unroll
-        for (int db = 0; db < 4; ++db) o[db] *= alpha;
-        need = false;
-      }
-      xa = fmaf(x[0][0], SCALE_LOG2, -mref);
-      pin(xa);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        if (jj + VLA < 16) read_v(jj + VLA);
-        const int u = jj >> 2, db = jj & 3;
-        const u32x4 av = {vlo[jj][0], vlo[jj][1], vhi[jj][0], vhi[jj][1]};
-        const u32x4 bp = {pw[4 * u], pw[4 * u + 1], pw[4 * u + 2], pw[4 * u + 3]};
-        o[db] = mfma32(as_bf16x8(av), as_bf16x8(bp), o[db]);
-        const float pv = fast_exp2(xa);
-        if (jj < 15) xa = fmaf(x[0][jj + 1], SCALE_LOG2, -mref);
-        if (jj > 0) {
-          lt += pp;
-          if ((jj - 1) & 1) {
-            pn[(jj - 1) >> 1] = pack_bf16(pe, pp);
-            pin(pn[(jj - 1) >> 1]);
-          } else {
-            pe = pp;
-            pin(pe);
-          }
-        }
-        pp = pv;
-        pin(pp);
+        for (int j = 0; j < KLA; ++j) kop[j] = ld_lds16(nxt + koff[j >> 1] + (j & 1) * 8192);
+        float pe = 0.f, pp = 0.f;
+        float xa = fmaf(s1[0], SCALE_LOG2, -mref);
         pin(xa);
-        pin(lt);
         __builtin_amdgcn_sched_barrier(0);
-      }
-      lt += pp;
-      pn[7] = pack_bf16(pe, pp);
-      if constexpr (SEG) {
-        if ((t + 1) % a.seg_tiles == 0 && t + 1 < n_tiles) {
-          // A chunk boundary: this pair's partial is complete, and the next
-          // pair starts exactly as a launch of its own would: zero state, the
-          // reference at the row max of its first tile (whose scores x already
-          // holds, masked), then key block 0 of that tile's P.
-          write_out(t / a.seg_tiles);
 #pragma unroll
-          for (int db = 0; db < 4; ++db) o[db] = (f32x16){};
-          m = kNegInf;
-          l = 0.f;
-          lt = 0.f;
-          move_to_max(x);
+        for (int j = 0; j < 16; ++j) {
+          if (j + KLA < 16) kop[j + KLA] = ld_lds16(nxt + koff[(j + KLA) >> 1] + ((j + KLA) & 1) * 8192);
+          if (j >= 16 - VLA) read_v(j - (16 - VLA));
+          x[j & 1] = mfma32(as_bf16x8(kop[j]), qf[j >> 1], x[j & 1]);
+          // slot j: exponent of score j, argument of score j+1, sum and pack of score j-1
+          const float pv = fast_exp2(xa);
+          if (j < 15) xa = fmaf(s1[j + 1], SCALE_LOG2, -mref);
+          if (j > 0) {
+            lt += pp;
+            if ((j - 1) & 1) {
+              pw[8 + ((j - 1) >> 1)] = pack_bf16(pe, pp);
+              pin(pw[8 + ((j - 1) >> 1)]);
+            } else {
+              pe = pp;
+              pin(pe);
+            }
+          }
+          pp = pv;
+          pin(pp);
+          pin(xa);
+          pin(lt);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        lt += pp;
+        pw[15] = pack_bf16(pe, pp);
+        mask_tile(x, t + 1);
+        // tile t is complete: keep it, or take the slow path
+        if (__any(!(lt <= kTwoTau) || m == kNegInf)) redo_tile(cur, t, pw);
+        l += lt;
+        lt = 0.f;
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- phase B: O^T += V(t)^T P(t)^T; key block 0 of P(t+1) ----
+        __builtin_amdgcn_s_setprio(0);
+        if (need) {
+#pragma unroll
+          for (int db = 0; db < 4; ++db) o[db] *= alpha;
           need = false;
+        }
+        xa = fmaf(x[0][0], SCALE_LOG2, -mref);
+        pin(xa);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int w = 0; w < 8; ++w) {
-            const float p0 = prob(x[0][2 * w]);
-            const float p1 = prob(x[0][2 * w + 1]);
-            pn[w] = pack_bf16(p0, p1);
+        for (int jj = 0; jj < 16; ++jj) {
+          if (jj + VLA < 16) read_v(jj + VLA);
+          const int u = jj >> 2, db = jj & 3;
+          const u32x4 av = {vlo[jj][0], vlo[jj][1], vhi[jj][0], vhi[jj][1]};
+          const u32x4 bp = {pw[4 * u], pw[4 * u + 1], pw[4 * u + 2], pw[4 * u + 3]};
+          o[db] = mfma32(as_bf16x8(av), as_bf16x8(bp), o[db]);
+          const float pv = fast_exp2(xa);
+          if (jj < 15) xa = fmaf(x[0][jj + 1], SCALE_LOG2, -mref);
+          if (jj > 0) {
+            lt += pp;
+            if ((jj - 1) & 1) {
+              pn[(jj - 1) >> 1] = pack_bf16(pe, pp);
+              pin(pn[(jj - 1) >> 1]);
+            } else {
+              pe = pp;
+              pin(pe);
+            }
+          }
+          pp = pv;
+          pin(pp);
+          pin(xa);
+          pin(lt);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        lt += pp;
+        pn[7] = pack_bf16(pe, pp);
+        if constexpr (SEG) {
+          if ((t + 1) % a.seg_tiles == 0 && t + 1 < n_tiles) {
+            // A chunk boundary: this pair's partial is complete, and the next
+            // pair starts exactly as a launch of its own would: zero state, the
+            // reference at the row max of its first tile (whose scores x already
+            // holds, masked), then key block 0 of that tile's P.
+            write_out(t / a.seg_tiles);
+#pragma unroll
+            for (int db = 0; db < 4; ++db) o[db] = (f32x16){};
+            m = kNegInf;
+            l = 0.f;
+            lt = 0.f;
+            move_to_max(x);
+            need = false;
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+              const float p0 = prob(x[0][2 * w]);
+              const float p1 = prob(x[0][2 * w + 1]);
+              pn[w] = pack_bf16(p0, p1);
+            }
           }
         }
+        // tile t+2 (fetched above) must have landed before any wave reads it
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      };
+      // six iterations per trip: three LDS stages times two register sets
+      static_assert(NST == 3, "the loop below is unrolled over three stages");
+      for (int t = 0; t < n_tiles; t += 2 * NST) {
+        iteration(t, std::integral_constant<int, 0>{}, snA, snB, pwA, pwB);
+        if (t + 1 < n_tiles) iteration(t + 1, std::integral_constant<int, 1>{}, snB, snA, pwB, pwA);
+        if (t + 2 < n_tiles) iteration(t + 2, std::integral_constant<int, 2>{}, snA, snB, pwA, pwB);
+        if (t + 3 < n_tiles) iteration(t + 3, std::integral_constant<int, 0>{}, snB, snA, pwB, pwA);
+        if (t + 4 < n_tiles) iteration(t + 4, std::integral_constant<int, 1>{}, snA, snB, pwA, pwB);
+        if (t + 5 < n_tiles) iteration(t + 5, std::integral_constant<int, 2>{}, snB, snA, pwB, pwA);
       }
-      // tile t+2 (fetched above) must have landed before any wave reads it
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    };
-    // six iterations per trip: three LDS stages times two register sets
-    static_assert(NST == 3, "the loop below is unrolled over three stages");
-    for (int t = 0; t < n_tiles; t += 2 * NST) {
-      iteration(t, std::integral_constant<int, 0>{}, snA, snB, pwA, pwB);
-      if (t + 1 < n_tiles) iteration(t + 1, std::integral_constant<int, 1>{}, snB, snA, pwB, pwA);
-      if (t + 2 < n_tiles) iteration(t + 2, std::integral_constant<int, 2>{}, snA, snB, pwA, pwB);
-      if (t + 3 < n_tiles) iteration(t + 3, std::integral_constant<int, 0>{}, snB, snA, pwB, pwA);
-      if (t + 4 < n_tiles) iteration(t + 4, std::integral_constant<int, 1>{}, snA, snB, pwA, pwB);
-      if (t + 5 < n_tiles) iteration(t + 5, std::integral_constant<int, 2>{}, snB, snA, pwB, pwA);
     }
   }
 
