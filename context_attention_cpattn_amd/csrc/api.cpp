@@ -703,12 +703,22 @@ cpattn_status cpattn_ring_prefill(const cpattn_tensor* q, const cpattn_tensor* k
     a.causal = cz ? 1 : 0;
     a.seg_tiles = (int32_t)(L.Ckv / 64);
     a.xcd_order = 0;  // launch order, heaviest owner first
+    // Each query tile merges its own partials when its walk is done (arrival
+    // order, the ring merge kernel's arithmetic), so no merge pass follows.
+    a.final_out = out->data;
+    a.final_bf16 = out->dtype == CPATTN_BF16;
+    a.pass_q = ord == CPATTN_PASS_Q ? 1 : 0;
+    a.f_sb = out->stride_b; a.f_ss = out->stride_s; a.f_sh = out->stride_h;
+    if (lse != nullptr) {
+      a.final_lse = static_cast<float*>(lse->data);
+      a.fl_sb = lse->stride_b; a.fl_ss = lse->stride_s; a.fl_sh = lse->stride_h;
+    }
     a.n_items = 0;
     for (int i = n_chunks - 1; i >= 0; --i)
       a.items[a.n_items++] = cpattn::Item{i, 0, L.slot0[i], (int32_t)owner_keys(L, i, cz)};
     const hipError_t e = launch_partial(a, q->dtype, (int)q->D, (int)L.Cq, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "ring prefill launch");
-    return ring_merge_impl(L, ord, workspace, out, lse, stream);
+    return ok();
   }
   // The workgroups of a launch are dealt to the XCDs in contiguous eighths of
   // the grid, so the diagonal pairs (half the work of a full pair under the

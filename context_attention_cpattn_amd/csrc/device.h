@@ -122,6 +122,44 @@ __device__ __forceinline__ RowOut row_out(float m2, float l, bool accumulate, fl
   return RowOut{(l > 0.f) ? wn * t / l : 0.f, wo * t, (mx + fast_log2(wn + wo)) * kLn2};
 }
 
+// The LSE merge of n partials of a row, one piece at a time so that every
+// kernel that merges rounds identically: with M the largest partial LSE,
+// partial c gets the weight w_c = exp(lse_c - M); den and acc sum w_c and
+// w_c O_c in partial order; the row is acc / den and its LSE M + ln(den).
+__device__ __forceinline__ float merge_weight(float lse, float M) { return fast_exp2((lse - M) * kLog2e); }
+__device__ __forceinline__ void merge_acc(f32x4& acc, float w, const f32x4& v) {
+  acc[0] = fmaf(w, v[0], acc[0]);
+  acc[1] = fmaf(w, v[1], acc[1]);
+  acc[2] = fmaf(w, v[2], acc[2]);
+  acc[3] = fmaf(w, v[3], acc[3]);
+}
+__device__ __forceinline__ float merge_inv(float den) { return (den > 0.f) ? 1.f / den : 0.f; }
+__device__ __forceinline__ float merged_lse(float M, float den) {
+  return (den > 0.f) ? M + fast_log2(den) * kLn2 : kNegInf;
+}
+
+// Four consecutive output values, as fp32 or rounded to bf16.
+__device__ __forceinline__ void store_row(void* out, bool out_bf16, int64_t off, const f32x4& r) {
+  if (out_bf16) {
+    const u32x2 pk = {pack_bf16(r[0], r[1]), pack_bf16(r[2], r[3])};
+    *reinterpret_cast<u32x2*>(static_cast<__bf16*>(out) + off) = pk;
+  } else {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + off) = r;
+  }
+}
+
+// The K/V chunk of the c-th partial to reach owner i, whose visible K/V
+// chunks are [0, n) (n >= i + 1: a Q chunk always sees its own K/V chunk).
+// Pass-KV sends K/V down the ring, so at step s owner i holds K/V chunk
+// (i - s) mod P: the visible ones arrive as i, i-1, ..., 0, then n-1, n-2,
+// ..., i+1.  Pass-Q sends Q, so at step s the rank holding K/V chunk
+// (i + s) mod P computes owner i's piece: i, i+1, ..., n-1, then 0, 1, ...,
+// i-1.  (Equal Q and K/V lengths under the causal mask give n = i + 1.)
+__device__ __forceinline__ int arrival_kv(bool pass_q, int i, int n, int c) {
+  if (pass_q) return c < n - i ? i + c : c - (n - i);
+  return c <= i ? i - c : n + i - c;
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup w runs on
 // XCD w % 8).  Give each XCD a contiguous range of logical tiles so tiles that
 // share K/V (adjacent heads of one query tile) share that XCD's L2.

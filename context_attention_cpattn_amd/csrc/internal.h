@@ -43,6 +43,14 @@ struct PartialLaunch {
   int32_t accumulate; // 1: merge into the (O, LSE) already at the destination (lse not null)
   int32_t seg_tiles;  // > 0: an item's keys form segments of this many 64-key tiles, each one
                       // written as its own partial to slot item.slot + segment (D = 128 BF16)
+  // With segments and final_out set, each query tile also merges its segments'
+  // partials once its walk is done, in the ring order's arrival order (pass_q),
+  // into row item.q_chunk * chunk_len + row of final_out (and final_lse).
+  void* final_out;
+  int32_t final_bf16, pass_q;
+  int64_t f_sb, f_ss, f_sh;
+  float* final_lse;           // may be null
+  int64_t fl_sb, fl_ss, fl_sh;
   Item items[kMaxItems];
 };
 

@@ -15,11 +15,12 @@
 namespace cpattn {
 namespace {
 
-// One row's merge, shared by both kernels so they round identically.  The
-// partials' LSEs give M first; then the O pieces are read in batches of 8
-// (all loads of a batch issued before any is used, for memory-level
-// parallelism) and accumulated in partial order.  o_at(c) / l_at(c) give the
-// c-th partial's 16 bytes of this thread and its LSE.
+// One row's merge, shared by both kernels (and built from the same pieces as
+// the chunk walk's merge tail) so they round identically.  The partials'
+// LSEs give M first; then the O pieces are read in batches of 8 (all loads
+// of a batch issued before any is used, for memory-level parallelism) and
+// accumulated in partial order.  o_at(c) / l_at(c) give the c-th partial's
+// 16 bytes of this thread and its LSE.
 template <class OAt, class LAt>
 __device__ __forceinline__ void merge_row(int n, OAt o_at, LAt l_at, f32x4& res, float& M, float& den) {
   M = kNegInf;
@@ -39,26 +40,13 @@ __device__ __forceinline__ void merge_row(int n, OAt o_at, LAt l_at, f32x4& res,
 #pragma unroll
       for (int u = 0; u < 8; ++u)
         if (c0 + u < n) {
-          const float w = fast_exp2((lw[u] - M) * kLog2e);
+          const float w = merge_weight(lw[u], M);
           den += w;
-          acc[0] = fmaf(w, v[u][0], acc[0]);
-          acc[1] = fmaf(w, v[u][1], acc[1]);
-          acc[2] = fmaf(w, v[u][2], acc[2]);
-          acc[3] = fmaf(w, v[u][3], acc[3]);
+          merge_acc(acc, w, v[u]);
         }
     }
   }
-  const float inv = (den > 0.f) ? 1.f / den : 0.f;
-  res = acc * inv;
-}
-
-__device__ __forceinline__ void store_row(void* out, bool out_bf16, int64_t off, const f32x4& r) {
-  if (out_bf16) {
-    const u32x2 pk = {pack_bf16(r[0], r[1]), pack_bf16(r[2], r[3])};
-    *reinterpret_cast<u32x2*>(static_cast<__bf16*>(out) + off) = pk;
-  } else {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + off) = r;
-  }
+  res = acc * merge_inv(den);
 }
 
 template <int D>
@@ -84,19 +72,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeLaunch a) {
       r, M, den);
   store_row(a.out, a.out_bf16, b * a.o_sb + s * a.o_ss + h * a.o_sh + 4 * part, r);
   if (a.out_lse != nullptr && part == 0)
-    a.out_lse[b * a.ol_sb + s * a.ol_ss + h * a.ol_sh] = (den > 0.f) ? M + fast_log2(den) * kLn2 : kNegInf;
-}
-
-// The c-th partial to reach owner i, whose visible K/V chunks are [0, n)
-// (n >= i + 1: a Q chunk always sees its own K/V chunk).  Pass-KV sends K/V
-// down the ring, so at step s owner i holds K/V chunk (i - s) mod P: the
-// visible ones arrive as i, i-1, ..., 0, then n-1, n-2, ..., i+1.  Pass-Q
-// sends Q, so at step s the rank holding K/V chunk (i + s) mod P computes
-// owner i's piece: i, i+1, ..., n-1, then 0, 1, ..., i-1.  (Equal Q and K/V
-// lengths under the causal mask give n = i + 1.)
-__device__ __forceinline__ int arrival_kv(bool pass_q, int i, int n, int c) {
-  if (pass_q) return c < n - i ? i + c : c - (n - i);
-  return c <= i ? i - c : n + i - c;
+    a.out_lse[b * a.ol_sb + s * a.ol_ss + h * a.ol_sh] = merged_lse(M, den);
 }
 
 template <int D>
@@ -125,7 +101,7 @@ __global__ __launch_bounds__(256) void ring_merge_kernel(const RingMergeLaunch a
   const int64_t sg = (int64_t)i * a.C + s;  // row of the full sequence
   store_row(a.out, a.out_bf16, b * a.o_sb + sg * a.o_ss + h * a.o_sh + 4 * part, res);
   if (a.out_lse != nullptr && part == 0)
-    a.out_lse[b * a.ol_sb + sg * a.ol_ss + h * a.ol_sh] = (den > 0.f) ? M + fast_log2(den) * kLn2 : kNegInf;
+    a.out_lse[b * a.ol_sb + sg * a.ol_ss + h * a.ol_sh] = merged_lse(M, den);
 }
 
 }  // namespace

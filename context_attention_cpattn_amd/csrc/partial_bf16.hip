@@ -431,13 +431,20 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
   float m = kNegInf;  // running reference (log2 domain) of this lane's row
   float l = 0.f;      // this lane's share of the row sum, relative to m
 
+  // With segments and a merge tail, the LSE of each segment's partial for this
+  // wave's rows is kept in LDS: 32 rows x 64 segments per wave, in the wave's
+  // own rows of the query tile area, which only this wave reads (once, in the
+  // prologue).
+  float* const seg_lse = reinterpret_cast<float*>(qsm) + wave * 32 * 64;
+
   // normalise and store this lane's row of segment `seg` (slot item.slot + seg)
-  auto write_out = [&](int seg) {
-    const float l_tot = pair32_sum(l);
+  // from the running reference m_ and row share l_
+  auto write_out = [&](int seg, float m_, float l_) {
+    const float l_tot = pair32_sum(l_);
     if (row < a.Sq) {
       const bool acc = a.accumulate != 0;
       float* const lps = lp != nullptr ? lp + seg * a.l_slot : nullptr;
-      const RowOut ro = row_out(m, l_tot, acc, acc ? lps[(int64_t)row * a.l_ss] : 0.f);
+      const RowOut ro = row_out(m_, l_tot, acc, acc ? lps[(int64_t)row * a.l_ss] : 0.f);
       float* orow = op + seg * a.o_slot + (int64_t)row * a.o_ss;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
@@ -454,6 +461,8 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
           *reinterpret_cast<f32x4*>(dst) = v4;
         }
       if (g == 0 && lps != nullptr) lps[(int64_t)row * a.l_ss] = ro.lse;
+      if constexpr (SEG)
+        if (g == 0 && a.final_out != nullptr) seg_lse[seg * 32 + l32] = ro.lse;
     }
   };
 
@@ -547,6 +556,12 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
     f32x16 snA[2], snB[2];
     uint32_t pwA[16], pwB[16];
     float lt = 0.f;     // this lane's partial sum of that tile
+    // A finished segment whose stores wait for the next iteration's fetch to be
+    // issued first, so the per-tile wait for that fetch does not also wait for
+    // them: its reference, row share and index (O stays in o until then).
+    bool pend = false;
+    float m_pend = 0.f, l_pend = 0.f;
+    int seg_pend = 0;
     bool need = false;  // O must be rescaled by alpha before the next PV
     float alpha = 1.f;
     float mref = 0.f;
@@ -642,6 +657,14 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
         // tile t+2 goes into the stage tile t-1 used
         const bool do_fetch = t + NST - 1 < n_tiles;
         if (do_fetch) fetch(SL);
+        if constexpr (SEG) {
+          if (pend) {
+            write_out(seg_pend, m_pend, l_pend);
+#pragma unroll
+            for (int db = 0; db < 4; ++db) o[db] = (f32x16){};
+            pend = false;
+          }
+        }
 
         u32x4 kop[16];
         u32x2 vlo[16], vhi[16];
@@ -733,13 +756,15 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
         pn[7] = pack_bf16(pe, pp);
         if constexpr (SEG) {
           if ((t + 1) % a.seg_tiles == 0 && t + 1 < n_tiles) {
-            // A chunk boundary: this pair's partial is complete, and the next
-            // pair starts exactly as a launch of its own would: zero state, the
-            // reference at the row max of its first tile (whose scores x already
-            // holds, masked), then key block 0 of that tile's P.
-            write_out(t / a.seg_tiles);
-#pragma unroll
-            for (int db = 0; db < 4; ++db) o[db] = (f32x16){};
+            // A chunk boundary: this pair's partial is complete (written at the
+            // start of the next iteration, O zeroed there before its first PV),
+            // and the next pair starts exactly as a launch of its own would:
+            // zero state, the reference at the row max of its first tile (whose
+            // scores x already holds, masked), then key block 0 of that tile's P.
+            pend = true;
+            m_pend = m;
+            l_pend = l;
+            seg_pend = t / a.seg_tiles;
             m = kNegInf;
             l = 0.f;
             lt = 0.f;
@@ -770,7 +795,7 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
   }
 
   const int last_seg = SEG && n_tiles > 0 ? (n_tiles - 1) / a.seg_tiles : 0;
-  write_out(last_seg);
+  write_out(last_seg, m, l);
   if constexpr (SEG) {
     // Segments past this query tile's last visible key hold pairs its rows see
     // nothing of (queries shorter than K/V put the last chunk's first keys after
@@ -781,7 +806,50 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
       for (int db = 0; db < 4; ++db) o[db] = (f32x16){};
       m = kNegInf;
       l = 0.f;
-      for (int seg = last_seg + 1; seg < n_seg; ++seg) write_out(seg);
+      for (int seg = last_seg + 1; seg < n_seg; ++seg) write_out(seg, m, l);
+    }
+    if (a.final_out != nullptr && row < a.Sq) {
+      // Merge tail: this lane's pieces of the n_seg partials it has just
+      // written, in the ring order's arrival order, with the arithmetic of the
+      // ring merge kernel (the same pieces in the same order: bit-identical).
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+      const int i = it.q_chunk;
+      const bool pq = a.pass_q != 0;
+      float M = kNegInf;
+      for (int c = 0; c < n_seg; ++c) M = fmaxf(M, seg_lse[c * 32 + l32]);
+      f32x4 acc[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) acc[k] = (f32x4){};
+      float den = 0.f;
+      const float* const orow = op + (int64_t)row * a.o_ss + 4 * g;
+      auto load_seg = [&](int j, f32x4 (&v)[16]) {
+        const float* src = orow + j * a.o_slot;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v[k] = *reinterpret_cast<const f32x4*>(src + (k >> 2) * 32 + 8 * (k & 3));
+      };
+      if (M != kNegInf) {
+        f32x4 cur[16], nxt[16];
+        int j = arrival_kv(pq, i, n_seg, 0);
+        load_seg(j, cur);
+        for (int c = 0; c < n_seg; ++c) {
+          const int jn = c + 1 < n_seg ? arrival_kv(pq, i, n_seg, c + 1) : j;
+          if (c + 1 < n_seg) load_seg(jn, nxt);
+          const float w = merge_weight(seg_lse[j * 32 + l32], M);
+          den += w;
+#pragma unroll
+          for (int k = 0; k < 16; ++k) merge_acc(acc[k], w, cur[k]);
+#pragma unroll
+          for (int k = 0; k < 16; ++k) cur[k] = nxt[k];
+          j = jn;
+        }
+      }
+      const float inv = merge_inv(den);
+      const int64_t grow = (int64_t)i * a.chunk_len + row;
+      const int64_t fo = b * a.f_sb + grow * a.f_ss + h * a.f_sh + 4 * g;
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        store_row(a.final_out, a.final_bf16 != 0, fo + (k >> 2) * 32 + 8 * (k & 3), acc[k] * inv);
+      if (g == 0 && a.final_lse != nullptr) a.final_lse[b * a.fl_sb + grow * a.fl_ss + h * a.fl_sh] = merged_lse(M, den);
     }
   }
 }
