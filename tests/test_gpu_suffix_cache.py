@@ -40,11 +40,11 @@ def suffix_reference(q, k, v, causal):
     return oracle.partial_attention(q, k, v, k.shape[1] - q.shape[1], 0, causal)
 
 
-# (B, Sq, Skv, P, Hq, Hkv, D, dtype): K/V chunks of a multiple of 64 up to 4096 keys take the
+# (B, Sq, Skv, P, Hq, Hkv, D, dtype): bf16 D = 128 with K/V chunks of a multiple of 64 keys takes the
 # per-owner walk, the others one work item per pair
 SUFFIX_CASES = [
     (1, 512, 2048, 4, 4, 1, 128, "bf16"),     # walk: 512-key chunks, 128-query chunks
-    (2, 300, 12480, 3, 4, 2, 128, "bf16"),    # per pair: 4160-key chunks, ragged 100-query chunks
+    (2, 300, 12480, 3, 4, 2, 128, "bf16"),    # walk: 4160-key chunks, ragged 100-query chunks
     (1, 200, 4000, 4, 2, 1, 128, "bf16"),     # per pair: 1000-key chunks (not a multiple of 64)
     (1, 1024, 1024, 8, 2, 1, 128, "bf16"),    # equal lengths through the same code
     (1, 64, 8192, 16, 8, 1, 128, "bf16"),     # walk: 4 queries per chunk, 512-key chunks
@@ -75,8 +75,9 @@ def test_suffix_ring_prefill(cp, case):
         d = (outs["pass_kv"][0] - outs["pass_q"][0]).abs().max().item()
         assert d <= (1e-5 if dt == "bf16" else 1e-6)
         # per-step launches + merge equal the whole ring bit for bit (with K/V chunks of a multiple of
-        # 64 up to 4096 keys the whole ring walks each owner's keys and writes every pair's partial at
-        # the chunk boundaries, empty ones included: the same partials as per-pair launches)
+        # 64 keys the whole ring walks each owner's keys, writes every pair's partial at the chunk
+        # boundaries, empty ones included, and merges them at the end of the walk: the same partials
+        # as per-pair launches, merged with the same arithmetic)
         for order in ("pass_kv", "pass_q"):
             banner("suffix ring steps", case, order, causal)
             ws = torch.empty(cp.ring_prefill_workspace_size(gq, P, causal, gk), dtype=torch.uint8, device=DEV)
