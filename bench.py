@@ -350,8 +350,16 @@ def main(argv=None) -> int:
                                 "merge": {"ms": round(merge_ms, 4), "GB/s": round(merge_bytes / (merge_ms * 1e-3) / 1e9, 1),
                                           "frac_hbm": round(merge_bytes / (merge_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                                           "algorithmic_bytes": merge_bytes}}
-    del ws
     log(f"[bench] ring with workspace {ms_w:.2f} ms (merge {merge_ms:.3f} ms)")
+
+    # ---- the whole ring as one call: per-owner walk, partials into the workspace, merged at the walk's end
+    ms_r = timed_reps(torch, stream, lambda: cp.ring_prefill(gq, gk, gv, P, "pass_kv", True, out=out, lse=lse,
+                                                             workspace=ws), max(3, args.steps // 2))
+    result["ring_prefill"] = {**tf(total_flops, ms_r), "launch": "ring_prefill: one launch, each owner's query "
+                              "tiles walk their visible K/V chunks writing every pair's partial, then merge them "
+                              "in arrival order"}
+    del ws
+    log(f"[bench] ring_prefill {ms_r:.2f} ms")
 
     # ---- fused: every owner walks its visible keys once, merge online, one launch
     ms_f = timed_reps(torch, stream, lambda: cp.ring_prefill_fused(gq, gk, gv, P, True, out=out, lse=lse),
@@ -374,7 +382,8 @@ def main(argv=None) -> int:
                                                                workspace=ws8), reps)
     ms8f = timed_reps(torch, stream, lambda: cp.ring_prefill_fused(*x, w8.n_chunks, True, out=o8, lse=l8), reps)
     result["gqa_8k"] = {"workload": w8.name, "order": "pass_kv", **tf(w8.flops(), ms8), "flop": w8.flops(),
-                        "launch": "ring_prefill: per-owner walk writing every pair's partial, then one merge",
+                        "launch": "ring_prefill: one launch, each owner's query tiles walk their visible K/V "
+                        "chunks writing every pair's partial, then merge them in arrival order",
                         "fused": tf(w8.flops(), ms8f)}
     log(f"[bench] 8K ring {ms8:.3f} ms, fused {ms8f:.3f} ms")
     del x, o8, l8, ws8
@@ -467,7 +476,8 @@ def main(argv=None) -> int:
                 log(f"[bench] {w1.name} {name} rep {i + 1}/3: {ts[-1]:.1f} ms")
             res1[name] = tf(w1.flops(), sorted(ts)[1])
         result["prefill_1m"] = {"workload": w1.name, "order": "pass_kv", "flop": w1.flops(), **res1["ring_prefill"],
-                                "launch": "ring_prefill: all pairs in one launch, then one merge",
+                                "launch": "ring_prefill: one launch, each owner's query tiles walk their visible "
+                                "K/V chunks writing every pair's partial, then merge them in arrival order",
                                 "fused": res1["fused"]}
         del x, o1, l1, ws1
         torch.cuda.empty_cache()
