@@ -855,22 +855,32 @@ cpattn_status cpattn_kv_cache_write(const cpattn_tensor* k, const cpattn_tensor*
   if (sh.S < C) return fail(CPATTN_ERR_INVALID_ARG, "shards hold %lld rows, a chunk has %lld", (long long)sh.S, (long long)C);
   if (C == 0 || k->B == 0 || k->H == 0) return ok();
   const int64_t eb = elem_bytes(k->dtype);
+  // K and V in one launch when they share strides (as tensors of one shape
+  // usually do) and their jobs fit; otherwise one launch each.
+  const bool together = 2 * n_chunks <= cpattn::kMaxMerge && k->stride_b == v->stride_b &&
+                        k->stride_s == v->stride_s && k->stride_h == v->stride_h &&
+                        k_shards[0].stride_b == v_shards[0].stride_b && k_shards[0].stride_s == v_shards[0].stride_s &&
+                        k_shards[0].stride_h == v_shards[0].stride_h;
+  cpattn::CopyLaunch c;
   for (int t = 0; t < 2; ++t) {
     const cpattn_tensor& src = t == 0 ? *k : *v;
     const cpattn_tensor* dst = t == 0 ? k_shards : v_shards;
-    cpattn::CopyLaunch c;
-    std::memset(&c, 0, sizeof c);
-    c.n_jobs = n_chunks;
-    c.elem_bytes = (int32_t)eb;
-    c.B = (int32_t)src.B; c.rows = (int32_t)C; c.H = (int32_t)src.H; c.D = (int32_t)src.D;
-    c.s_sb = src.stride_b; c.s_ss = src.stride_s; c.s_sh = src.stride_h;
-    c.d_sb = dst[0].stride_b; c.d_ss = dst[0].stride_s; c.d_sh = dst[0].stride_h;
-    for (int r = 0; r < n_chunks; ++r) {
-      c.src[r] = static_cast<const char*>(src.data) + r * C * src.stride_s * eb;
-      c.dst[r] = dst[r].data;
+    if (t == 0 || !together) {
+      std::memset(&c, 0, sizeof c);
+      c.elem_bytes = (int32_t)eb;
+      c.B = (int32_t)src.B; c.rows = (int32_t)C; c.H = (int32_t)src.H; c.D = (int32_t)src.D;
+      c.s_sb = src.stride_b; c.s_ss = src.stride_s; c.s_sh = src.stride_h;
+      c.d_sb = dst[0].stride_b; c.d_ss = dst[0].stride_s; c.d_sh = dst[0].stride_h;
     }
-    const hipError_t e = cpattn::launch_copy(c, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "cache write launch");
+    for (int r = 0; r < n_chunks; ++r) {
+      c.src[c.n_jobs] = static_cast<const char*>(src.data) + r * C * src.stride_s * eb;
+      c.dst[c.n_jobs] = dst[r].data;
+      ++c.n_jobs;
+    }
+    if (t == 1 || !together) {
+      const hipError_t e = cpattn::launch_copy(c, static_cast<hipStream_t>(stream));
+      if (e != hipSuccess) return hip_fail(e, "cache write launch");
+    }
   }
   return ok();
 }
