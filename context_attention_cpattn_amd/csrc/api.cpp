@@ -680,7 +680,7 @@ cpattn_status cpattn_ring_prefill(const cpattn_tensor* q, const cpattn_tensor* k
   // On one device the pairs of all ring steps are independent, so they go
   // out together; each lands in its own slot, and the merge reads the slots
   // in the ring order's arrival order.
-  if (q->dtype == CPATTN_BF16 && q->D == 128 && L.Ckv % 64 == 0) {
+  if (q->dtype == CPATTN_BF16 && q->D == 128 && L.Ckv % 64 == 0 && L.Ckv <= 16384) {
     // K/V chunks of a multiple of 64 tokens: one work item per owner whose
     // query tile walks every key it sees in one pass (as in the fused
     // prefill), writing each K/V chunk's partial to that pair's slot at the
@@ -689,6 +689,9 @@ cpattn_status cpattn_ring_prefill(const cpattn_tensor* q, const cpattn_tensor* k
     // workgroup prologue per pair -- and merging them at the end of the walk.
     // 8K tokens in 1024-token chunks: 0.357 -> 0.326 ms against per-pair
     // launches and a merge pass; 128K in 8192-token chunks: 60.1 -> 57.7 ms.
+    // Longer chunks amortise a pair's prologue over more tiles than the
+    // walk's boundary code costs (1M in 131072-token chunks: per-pair 0.8%
+    // faster), so they launch per pair.
     cpattn::PartialLaunch a = base_partial(*q, *k, *v);
     a.o = static_cast<float*>(workspace);
     a.lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.o_bytes);

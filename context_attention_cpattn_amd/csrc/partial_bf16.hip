@@ -540,9 +540,13 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
       ++n_fetched;
     };
 
+    // The masked tiles (diagonal and block end), the slow path of the lazy
+    // reference and the rescale after it are rare: marked unlikely, their code
+    // is laid out after the loop, so the six unrolled iterations' common path
+    // stays compact (~450 instructions each instead of ~830; +0.5-1%).
     auto mask_tile = [&](f32x16 (&sc)[2], int t) {
       const int n0 = t * BN;
-      if (n0 + BN > Sk || (a.causal && dpos + n0 + BN - 1 > r0)) {
+      if (__builtin_expect(n0 + BN > Sk || (a.causal && dpos + n0 + BN - 1 > r0), 0)) {
         int lim = Sk - n0;
         if (a.causal) lim = min(lim, row - dpos - n0 + 1);
         mask_block(sc, max(0, min(lim, BN)), g);
@@ -562,6 +566,7 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
     bool pend = false;
     float m_pend = 0.f, l_pend = 0.f;
     int seg_pend = 0;
+    int seg_left = a.seg_tiles, seg_idx = 0;  // tiles left in the current segment, its index
     bool need = false;  // O must be rescaled by alpha before the next PV
     float alpha = 1.f;
     float mref = 0.f;
@@ -712,14 +717,14 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
         pw[15] = pack_bf16(pe, pp);
         mask_tile(x, t + 1);
         // tile t is complete: keep it, or take the slow path
-        if (__any(!(lt <= kTwoTau) || m == kNegInf)) redo_tile(cur, t, pw);
+        if (__builtin_expect(__any(!(lt <= kTwoTau) || m == kNegInf), 0)) redo_tile(cur, t, pw);
         l += lt;
         lt = 0.f;
         __builtin_amdgcn_sched_barrier(0);
 
         // ---- phase B: O^T += V(t)^T P(t)^T; key block 0 of P(t+1) ----
         __builtin_amdgcn_s_setprio(0);
-        if (need) {
+        if (__builtin_expect(need, 0)) {
 #pragma unroll
           for (int db = 0; db < 4; ++db) o[db] *= alpha;
           need = false;
@@ -755,7 +760,11 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
         lt += pp;
         pn[7] = pack_bf16(pe, pp);
         if constexpr (SEG) {
-          if ((t + 1) % a.seg_tiles == 0 && t + 1 < n_tiles) {
+          if (--seg_left == 0) {
+            seg_left = a.seg_tiles;
+            seg_pend = seg_idx++;
+          }
+          if (seg_left == a.seg_tiles && t + 1 < n_tiles) {
             // A chunk boundary: this pair's partial is complete (written at the
             // start of the next iteration, O zeroed there before its first PV),
             // and the next pair starts exactly as a launch of its own would:
@@ -764,7 +773,6 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
             pend = true;
             m_pend = m;
             l_pend = l;
-            seg_pend = t / a.seg_tiles;
             m = kNegInf;
             l = 0.f;
             lt = 0.f;

@@ -183,9 +183,10 @@ def test_ring_merge_follows_arrival_order(cp, P, order, causal, C):
 @pytest.mark.parametrize("P,C,B,Hkv,order,causal", [(64, 64, 1, 1, "pass_kv", True), (8, 64, 2, 2, "pass_q", False),
                                                    (4, 320, 2, 2, "pass_kv", True), (3, 4096, 1, 1, "pass_q", True)])
 def test_ring_prefill_chunk_walk(cp, P, C, B, Hkv, order, causal):
-    """Chunks of a multiple of 64 tokens: the driver's per-owner walk that writes every pair's
-    partial at the chunk boundary and merges them at its end, against the oracle; 64-token chunks
-    put a boundary after every tile, and 64 of them use every segment slot of the merge tail."""
+    """Chunks of a multiple of 64 tokens (up to 16384): the driver's per-owner walk that writes
+    every pair's partial at the chunk boundary and merges them at its end, against the oracle;
+    64-token chunks put a boundary after every tile, and 64 of them use every segment slot of the
+    merge tail."""
     S, H = C * P, 4
     q = draw(131 + P, (B, S, H, 128), torch.bfloat16, 0)
     k = draw(131 + P, (B, S, Hkv, 128), torch.bfloat16, 1)

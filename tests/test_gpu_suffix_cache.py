@@ -40,8 +40,8 @@ def suffix_reference(q, k, v, causal):
     return oracle.partial_attention(q, k, v, k.shape[1] - q.shape[1], 0, causal)
 
 
-# (B, Sq, Skv, P, Hq, Hkv, D, dtype): bf16 D = 128 with K/V chunks of a multiple of 64 keys takes the
-# per-owner walk, the others one work item per pair
+# (B, Sq, Skv, P, Hq, Hkv, D, dtype): bf16 D = 128 with K/V chunks of a multiple of 64 keys (up to
+# 16384) takes the per-owner walk, the others one work item per pair
 SUFFIX_CASES = [
     (1, 512, 2048, 4, 4, 1, 128, "bf16"),     # walk: 512-key chunks, 128-query chunks
     (2, 300, 12480, 3, 4, 2, 128, "bf16"),    # walk: 4160-key chunks, ragged 100-query chunks
@@ -74,10 +74,10 @@ def test_suffix_ring_prefill(cp, case):
         assert torch.equal(outs["auto"][0], outs[chosen][0]) and torch.equal(outs["auto"][1], outs[chosen][1])
         d = (outs["pass_kv"][0] - outs["pass_q"][0]).abs().max().item()
         assert d <= (1e-5 if dt == "bf16" else 1e-6)
-        # per-step launches + merge equal the whole ring bit for bit (with K/V chunks of a multiple of
-        # 64 keys the whole ring walks each owner's keys, writes every pair's partial at the chunk
-        # boundaries, empty ones included, and merges them at the end of the walk: the same partials
-        # as per-pair launches, merged with the same arithmetic)
+        # per-step launches + merge equal the whole ring bit for bit (with K/V chunks of a multiple
+        # of 64 keys up to 16384 the whole ring walks each owner's keys, writes every pair's partial
+        # at the chunk boundaries, empty ones included, and merges them at the end of the walk: the
+        # same partials as per-pair launches, merged with the same arithmetic)
         for order in ("pass_kv", "pass_q"):
             banner("suffix ring steps", case, order, causal)
             ws = torch.empty(cp.ring_prefill_workspace_size(gq, P, causal, gk), dtype=torch.uint8, device=DEV)
