@@ -108,7 +108,7 @@ def pmc_values() -> dict:
 
 def trace_values() -> dict:
     """Entries of the committed kernel-trace summary of the current kernel sources."""
-    return _summary_values(TRACE_FILE, keep_text=("box_host", "box_gpu_uuid"))
+    return _summary_values(TRACE_FILE, keep_text=("machine_host", "machine_gpu_uuid"))
 
 
 def read_pmc_summary():
@@ -165,7 +165,7 @@ def cpu_baseline(w, q, k, v, seconds: float):
                       f"threads"}
 
 
-def box_id(torch) -> dict:
+def machine_id(torch) -> dict:
     import socket
     props = torch.cuda.get_device_properties(0)
     uuid = str(getattr(props, "uuid", "")) or None
@@ -216,7 +216,7 @@ def main(argv=None) -> int:
                     help="FETCH_DIR WRITE_DIR [CLOCK_DIR [SQ_DIR [RDREQ_DIR]]]: HBM traffic (shader clock, "
                          "MFMA busy fraction, read bytes by request size) from rocprofv3 --pmc runs")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"),
-                    help="kernel-trace summary of the headline kernel beside a plain bench line of the same box")
+                    help="kernel-trace summary of the headline kernel beside a plain bench line of the same machine")
     args = ap.parse_args(argv)
 
     if args.summarize_pmc:
@@ -237,9 +237,9 @@ def main(argv=None) -> int:
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    box = box_id(torch)
+    machine = machine_id(torch)
     w = si.WORKLOADS[PREFILL]
-    log(f"[bench] {box['device']} on {box['host']}, {cp.version()}; drawing {w.name} inputs")
+    log(f"[bench] {machine['device']} on {machine['host']}, {cp.version()}; drawing {w.name} inputs")
     q, k, v = si.make_qkv(w)
     gq, gk, gv = q.to(dev), k.to(dev), v.to(dev)
     P = w.n_chunks
@@ -284,13 +284,13 @@ def main(argv=None) -> int:
                 "kernel": "partial_bf16_d128_kernel<false> (accumulating ring step)", "launches_per_step": P,
                 "avg_launch_ms": round(avg_launch_ms, 4), "algorithmic_flop_per_launch": total_flops / P,
                 "basis": "HIP events around every ring-step launch of the timed steps, on the stream the library "
-                         "launches on; this run's box",
-                "box": box}
+                         "launches on; this run's machine",
+                "machine": machine}
     if trace:
-        # the committed kernel trace of the same kernel source and launch pattern, with the box it ran on
+        # the committed kernel trace of the same kernel source and launch pattern, with the machine it ran on
         roofline.update({"frac_profiled": trace.get("frac_profiled"),
                          "avg_launch_ms_profiled": trace.get("partial_kernel_avg_ms"),
-                         "profiled_box": trace.get("box_host"),
+                         "profiled_machine": trace.get("machine_host"),
                          "profiled_source": "profiles/partial_bf16_prefill_s128k_p16_trace.txt"})
     if sclk:
         roofline.update({"sclk_ghz_profiled": sclk, "mfma_busy_fraction_profiled": mfma_busy,
@@ -633,7 +633,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, clock_dir: str | None = None, 
 
 def summarize_trace(trace_dir: str, bench_json: str) -> int:
     """Kernel-trace summary of the headline kernel (``rocprofv3 --kernel-trace --stats`` of the
-    headline-only bench) next to the plain bench line taken in the same call on the same box."""
+    headline-only bench) next to the plain bench line taken in the same run on the same machine."""
     w = _prefill_workload()
     stats = {}
     for path in glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True):
@@ -652,14 +652,14 @@ def summarize_trace(trace_dir: str, bench_json: str) -> int:
     os.makedirs(os.path.dirname(TRACE_FILE), exist_ok=True)
     with open(TRACE_FILE, "w") as f:
         f.write("# Kernel trace of the headline: 128K-token Pass-KV ring, 16 accumulating ring-step launches per step.\n")
-        f.write("# On the MI355X box, from /tmp with TMPDIR=/tmp, R = repository root:\n")
-        f.write(f"#   rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/trace -o kt -- "
+        f.write("# On the MI355X machine, from /tmp with TMPDIR=/tmp, R = repository root, OUT = an output directory:\n")
+        f.write(f"#   rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/trace -o kt -- "
                 f"{PROFILE_CMD} --steps 5 --warmup 1\n")
-        f.write(f"#   python bench.py --summarize-trace gpurun_out/trace gpurun_out/bench_plain.json\n")
-        f.write("# where gpurun_out/bench_plain.json is the plain `python bench.py` line of the same call (same box).\n")
+        f.write(f"#   python bench.py --summarize-trace $OUT/trace $OUT/bench_plain.json\n")
+        f.write("# where $OUT/bench_plain.json is the plain `python bench.py` line of the same run (same machine).\n")
         f.write(f"kernel_source_sha256_16: {kernel_hash()}\n")
-        f.write(f"box_host: {line['roofline'].get('box', {}).get('host')}\n")
-        f.write(f"box_gpu_uuid: {line['roofline'].get('box', {}).get('gpu_uuid')}\n")
+        f.write(f"machine_host: {line['roofline'].get('machine', {}).get('host')}\n")
+        f.write(f"machine_gpu_uuid: {line['roofline'].get('machine', {}).get('gpu_uuid')}\n")
         f.write(f"partial_kernel_dispatches: {calls}\n")
         f.write(f"partial_kernel_avg_ms: {avg_ns / 1e6:.4f}\n")
         f.write(f"flop_per_launch: {flop_launch:.6e}\n")

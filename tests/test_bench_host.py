@@ -70,7 +70,7 @@ def test_counter_summary_scales_by_the_copy_kernel(tmp_path, monkeypatch):
 
 def test_trace_summary_and_its_readback(tmp_path, monkeypatch):
     """The kernel-trace summary: average partial-kernel launch -> TFLOP/s and fraction of the dense
-    peak, beside the plain bench line of the same box; read back only for the same kernel sources."""
+    peak, beside the plain bench line of the same machine; read back only for the same kernel sources."""
     import json
     out = tmp_path / "trace.txt"
     monkeypatch.setattr(bench, "TRACE_FILE", str(out))
@@ -83,11 +83,11 @@ def test_trace_summary_and_its_readback(tmp_path, monkeypatch):
         wr.writerow(["decode_stream_kernel<128>(args)", 10, 3.3e6, 3.3e5, 1.0, 3e5, 4e5, 1.0])
     bj = tmp_path / "b.json"
     bj.write_text(json.dumps({"ms_per_step": 57.0, "value": 1234.5,
-                              "roofline": {"avg_launch_ms": 3.45, "frac": 0.51, "box": {"host": "boxA", "gpu_uuid": "u"}}}))
+                              "roofline": {"avg_launch_ms": 3.45, "frac": 0.51, "machine": {"host": "hostA", "gpu_uuid": "u"}}}))
     assert bench.summarize_trace(str(d), str(bj)) == 0
     w = si.WORKLOADS["prefill_bf16_s128k_p16"]
     tv = bench.trace_values()
-    assert tv["box_host"] == "boxA"
+    assert tv["machine_host"] == "hostA"
     assert tv["partial_kernel_avg_ms"] == pytest.approx(3.5)
     assert tv["frac_profiled"] == pytest.approx(w.flops() / 16 / 3.5e-3 / 1e12 / bench.PEAK_BF16_TFLOPS, abs=1e-4)
     assert tv["trace_kernel_ms_per_step"] == pytest.approx(56.0)
