@@ -281,7 +281,7 @@ def main(argv=None) -> int:
     trace = trace_values()
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "kernel": "partial_bf16_d128_kernel<false> (accumulating ring step)", "launches_per_step": P,
+                "kernel": "partial_bf16_fast_kernel<128, false> (accumulating ring step)", "launches_per_step": P,
                 "avg_launch_ms": round(avg_launch_ms, 4), "algorithmic_flop_per_launch": total_flops / P,
                 "basis": "HIP events around every ring-step launch of the timed steps, on the stream the library "
                          "launches on; this run's machine",
@@ -551,8 +551,8 @@ def summarize_pmc(fetch_dir: str, write_dir: str, clock_dir: str | None = None, 
     GRBM_GUI_ACTIVE, also the shader clock the partial kernel ran at; with a fourth run of
     GRBM_GUI_ACTIVE and SQ counters, the MFMA busy fraction and the instruction mix."""
     fr, wr = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
-    f_k, nf = _per_dispatch(fr, "FETCH_SIZE", "partial_bf16_d128_kernel")
-    w_k, nw = _per_dispatch(wr, "WRITE_SIZE", "partial_bf16_d128_kernel")
+    f_k, nf = _per_dispatch(fr, "FETCH_SIZE", "partial_bf16_fast_kernel")
+    w_k, nw = _per_dispatch(wr, "WRITE_SIZE", "partial_bf16_fast_kernel")
     # the copy kernel is torch's x * 1.0 over 1 GiB (MulFunctor); the fill that creates its
     # source reads nothing and must not enter the calibration
     f_c, _ = _per_dispatch(fr, "FETCH_SIZE", "MulFunctor")
@@ -565,7 +565,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, clock_dir: str | None = None, 
     write_b = w_k * 1024.0 * w_scale
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
-        f.write("# HBM traffic of partial_bf16_d128_kernel per launch on the 128K-token workload, Pass-KV\n")
+        f.write("# HBM traffic of partial_bf16_fast_kernel<128, false> per launch on the 128K-token workload, Pass-KV\n")
         f.write("# accumulating ring steps, from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs of:\n")
         f.write(f"#   {PROFILE_CMD} --steps 1 --warmup 0 --calibrate-copy\n")
         f.write("# (every partial launch of that run is one Pass-KV ring step)\n")
@@ -596,20 +596,20 @@ def summarize_pmc(fetch_dir: str, write_dir: str, clock_dir: str | None = None, 
             rr = _pmc_rows(rdreq_dir)
             f.write("# cross-check from a run with TCC_EA0_RDREQ_{,128B_,64B_,32B_}sum: bytes read = 128/64/32 x\n"
                     "# the requests of each size (no calibration; 'other' = requests of none of those sizes)\n")
-            for label, part in (("partial", "partial_bf16_d128_kernel"), ("decode", "decode_stream_kernel"),
+            for label, part in (("partial", "partial_bf16_fast_kernel"), ("decode", "decode_stream_kernel"),
                                 ("ring_merge", "ring_merge_kernel"), ("copy", "MulFunctor")):
                 rb, other = _read_bytes_by_size(rr, part)
                 if rb is not None:
                     f.write(f"{label}_read_bytes_by_request_size: {rb:.0f} (other requests: {other:.0f})\n")
         if clock_dir:
             cr = _pmc_rows(clock_dir)
-            ck, cc = _clock_ghz(cr, "partial_bf16_d128_kernel"), _clock_ghz(cr, "MulFunctor")
+            ck, cc = _clock_ghz(cr, "partial_bf16_fast_kernel"), _clock_ghz(cr, "MulFunctor")
             f.write("# shader clock from a third run with --pmc GRBM_GUI_ACTIVE: busy clocks / 8 XCDs / dispatch time\n")
             f.write(f"sclk_ghz_partial_kernel: {ck:.3f}\n")
             f.write(f"sclk_ghz_copy_kernel: {cc:.3f}\n")
         if sq_dir:
             sr = _pmc_rows(sq_dir)
-            k = "partial_bf16_d128_kernel"
+            k = "partial_bf16_fast_kernel"
             tot = {}
             for name in ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_MFMA",
                          "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE"):
@@ -640,9 +640,9 @@ def summarize_trace(trace_dir: str, bench_json: str) -> int:
         with open(path, newline="") as f:
             for r in csv.DictReader(f):
                 stats[r["Name"]] = (int(r["Calls"]), float(r["AverageNs"]), float(r["TotalDurationNs"]))
-    part = [(n, v) for n, v in stats.items() if "partial_bf16_d128_kernel" in n]
+    part = [(n, v) for n, v in stats.items() if "partial_bf16_fast_kernel" in n]
     if not part:
-        raise SystemExit(f"no partial_bf16_d128_kernel dispatches in {trace_dir}")
+        raise SystemExit(f"no partial_bf16_fast_kernel dispatches in {trace_dir}")
     calls = sum(v[0] for _, v in part)
     avg_ns = sum(v[2] for _, v in part) / calls
     line = json.loads([ln for ln in open(bench_json) if ln.strip().startswith("{")][-1])

@@ -680,7 +680,7 @@ cpattn_status cpattn_ring_prefill(const cpattn_tensor* q, const cpattn_tensor* k
   // On one device the pairs of all ring steps are independent, so they go
   // out together; each lands in its own slot, and the merge reads the slots
   // in the ring order's arrival order.
-  if (q->dtype == CPATTN_BF16 && q->D == 128 && L.Ckv % 64 == 0 && L.Ckv <= 16384) {
+  if (q->dtype == CPATTN_BF16 && (q->D == 128 || q->D == 64) && L.Ckv % 64 == 0 && L.Ckv <= 16384) {
     // K/V chunks of a multiple of 64 tokens: one work item per owner whose
     // query tile walks every key it sees in one pass (as in the fused
     // prefill), writing each K/V chunk's partial to that pair's slot at the

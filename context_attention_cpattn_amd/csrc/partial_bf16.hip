@@ -8,20 +8,17 @@
 // Defines LLM Serving Cost"), so the two contractions run on MFMA and the
 // softmax bookkeeping is kept per lane.
 //
-// Orientation (both kernels): each wave computes S^T = K Q^T (keys on the
+// Orientation: each wave computes S^T = K Q^T (keys on the
 // MFMA rows, its 32 queries on the columns), so a lane holds scores of ONE
 // query.  Row reductions are in-lane plus one exchange with the lane 32
 // away, and the probabilities come out in the B-operand layout of the second
 // product O^T = V^T P^T, so P never leaves registers.
 //
 // Softmax runs in base 2 with the 1/sqrt(D) scale folded into one FMA.  The
-// running reference is only raised when scores exceed it by more than kTau
+// running reference is only raised when scores exceed it by more than 8
 // (2^8 in probability), so most tiles skip the O rescale; probabilities stay
 // <= 2^8, well inside bf16/fp32 range, and the result is exact in real
 // arithmetic because the final normalisation uses the same reference.
-//
-// D = 64: 4 waves = 128 query rows per workgroup, K/V staged through LDS by
-// registers (V transposed on the way in).  D = 128: the kernel further down.
 #include <type_traits>
 
 #include "device.h"
@@ -30,274 +27,10 @@
 namespace cpattn {
 namespace {
 
-constexpr float kTau = 8.0f;
-constexpr float kTwoTau = 256.0f;  // 2^kTau
-
-template <int D>
-struct Cfg {
-  static constexpr int BM = 128;             // query rows per workgroup
-  static constexpr int BN = 8192 / D;        // keys per tile (64 for D=128, 128 for D=64)
-  static constexpr int DCH = D / 8;          // 16-byte chunks per K/V row
-  static constexpr int NKB = BN / 32;        // 32-key blocks per tile
-  static constexpr int NDS = D / 16;         // k-steps of S^T = K Q^T
-  static constexpr int NDB = D / 32;         // 32-wide column blocks of O
-  static constexpr int KBYTES = BN * D * 2;  // one K tile (= one V^T tile)
-  static constexpr int STAGE = 2 * KBYTES;
-  static constexpr int KPT = BN * DCH / 256; // K chunks loaded per thread
-  static constexpr int VROW = BN * 2;        // bytes of one V^T row (one d)
-  static constexpr float SCALE_LOG2 = (D == 64) ? 0.18033688011112042f : 0.12751743082459868f;
-};
-static_assert(Cfg<128>::KPT == 4 && Cfg<64>::KPT == 4, "tile shape");
-static_assert(Cfg<128>::BN / 4 * Cfg<128>::DCH == 256 && Cfg<64>::BN / 4 * Cfg<64>::DCH == 256, "V split");
-
-// XOR swizzles keeping both the tile stores and the MFMA operand reads free
-// of LDS bank conflicts.
-template <int D>
-__device__ __forceinline__ int k_swz(int key, int ch) { return ch ^ (key & (Cfg<D>::DCH - 1)); }
-__device__ __forceinline__ int v_swz(int d) { return (d ^ (d >> 3)) & 15; }
-
-template <int D>
-__global__ __launch_bounds__(256) void partial_bf16_kernel(const PartialLaunch a, const int n_qtiles) {
-  using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int l32 = lane & 31;
-  const int g = lane >> 5;
-
-  // ---- which (item, query tile, batch, head) this workgroup computes
-  const int bh = a.B * a.Hq;
-  const int per_item = bh * n_qtiles;
-  const int L = (a.xcd_order ? xcd_logical_block(blockIdx.x, per_item * a.n_items) : (int)blockIdx.x);
-  const int item = L / per_item;
-  int rem = L - item * per_item;
-  const int qt = n_qtiles - 1 - rem / bh;  // later (heavier under the mask) tiles first
-  rem = rem % bh;
-  const int b = rem / a.Hq;
-  const int h = rem - b * a.Hq;
-  const int kvh = h / a.G;
-  const Item it = a.items[item];
-  const int Sk = it.sk > 0 ? it.sk : a.Sk;  // keys of this item's K/V block
-
-  const __bf16* qp = static_cast<const __bf16*>(a.q) + b * a.q_sb + h * a.q_sh +
-                     (int64_t)it.q_chunk * a.chunk_len * a.q_ss;
-  const __bf16* kp = static_cast<const __bf16*>(a.k) + b * a.k_sb + kvh * a.k_sh +
-                     (int64_t)it.kv_chunk * a.kv_chunk_len * a.k_ss;
-  const __bf16* vp = static_cast<const __bf16*>(a.v) + b * a.v_sb + kvh * a.v_sh +
-                     (int64_t)it.kv_chunk * a.kv_chunk_len * a.v_ss;
-  float* op = a.o + it.slot * a.o_slot + b * a.o_sb + h * a.o_sh;
-  float* lp = a.lse != nullptr ? a.lse + it.slot * a.l_slot + b * a.l_sb + h * a.l_sh : nullptr;  // LSE optional
-  const int64_t qpos0 = a.q_pos0 + (int64_t)it.q_chunk * a.chunk_len;
-  const int64_t kvpos0 = a.kv_pos0 + (int64_t)it.kv_chunk * a.kv_chunk_len;
-
-  const int m0 = qt * C::BM;
-  const int r0 = m0 + wave * 32;  // first row of this wave
-  const int row = r0 + l32;       // this lane's query row
-
-  // keys [0, n_end) can be visible to some row of this workgroup
-  int n_end = Sk;
-  if (a.causal) {
-    const int64_t last_row = (int64_t)min(m0 + C::BM, a.Sq) - 1;
-    const int64_t lim = qpos0 + last_row - kvpos0 + 1;
-    n_end = (int)max<int64_t>(0, min<int64_t>(Sk, lim));
-  }
-  const int n_tiles = (n_end + C::BN - 1) / C::BN;
-
-  f32x16 oacc[C::NDB];
-#pragma unroll
-  for (int db = 0; db < C::NDB; ++db) oacc[db] = (f32x16){};
-  float m_run = kNegInf;
-  float l_run = 0.f;
-
-  if (n_tiles > 0) {
-    // Q fragments, B operand of S^T = K Q^T: column = this lane's row,
-    // k-slots = d in [16 s + 8 g, 16 s + 8 g + 8).
-    bf16x8 qf[C::NDS];
-    {
-      const bool ok = row < a.Sq;
-      const __bf16* qr = qp + (int64_t)row * a.q_ss + 8 * g;
-#pragma unroll
-      for (int s = 0; s < C::NDS; ++s) qf[s] = ok ? as_bf16x8(ld_global16(qr + 16 * s)) : (bf16x8){};
-    }
-
-    u32x4 kreg[C::KPT];
-    u32x4 vreg[4];
-    const int vkg = tid / C::DCH;  // this thread's 4-key group of the V tile
-    const int vch = tid % C::DCH;  // and its 16-byte d chunk
-
-    auto load_tile = [&](int t) {
-      const int n0 = t * C::BN;
-#pragma unroll
-      for (int i = 0; i < C::KPT; ++i) {
-        const int idx = tid + 256 * i;
-        const int key = idx / C::DCH, ch = idx % C::DCH;
-        kreg[i] = (n0 + key < Sk) ? ld_global16(kp + (int64_t)(n0 + key) * a.k_ss + ch * 8) : (u32x4){};
-      }
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int key = n0 + 4 * vkg + kk;
-        vreg[kk] = (key < Sk) ? ld_global16(vp + (int64_t)key * a.v_ss + vch * 8) : (u32x4){};
-      }
-    };
-    auto store_tile = [&](int stage) {
-      uint8_t* ks = smem + stage * C::STAGE;
-      uint8_t* vs = ks + C::KBYTES;
-#pragma unroll
-      for (int i = 0; i < C::KPT; ++i) {
-        const int idx = tid + 256 * i;
-        const int key = idx / C::DCH, ch = idx % C::DCH;
-        st_lds16(ks + key * (D * 2) + (k_swz<D>(key, ch) << 4), kreg[i]);
-      }
-      // 4 keys x 8 d -> for each d, the 4 keys' values side by side
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int de = vch * 8 + 2 * w;
-        const int dodd = de + 1;
-        const u32x2 ev = {pack_lo16(vreg[0][w], vreg[1][w]), pack_lo16(vreg[2][w], vreg[3][w])};
-        const u32x2 od = {pack_hi16(vreg[0][w], vreg[1][w]), pack_hi16(vreg[2][w], vreg[3][w])};
-        st_lds8(vs + de * C::VROW + ((vkg ^ v_swz(de)) << 3), ev);
-        st_lds8(vs + dodd * C::VROW + ((vkg ^ v_swz(dodd)) << 3), od);
-      }
-    };
-
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-
-    for (int t = 0; t < n_tiles; ++t) {
-      const bool has_next = (t + 1) < n_tiles;
-      if (has_next) load_tile(t + 1);
-
-      const uint8_t* ks = smem + (t & 1) * C::STAGE;
-      const uint8_t* vs = ks + C::KBYTES;
-      const int n0 = t * C::BN;
-      const bool wave_active = (r0 < a.Sq) && (!a.causal || kvpos0 + n0 <= qpos0 + r0 + 31);
-
-      if (wave_active) {
-        // ---- S^T = K Q^T for this tile: NKB blocks of 32 keys x 32 queries
-        f32x16 sacc[C::NKB];
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb) {
-          const int key = kb * 32 + l32;
-          const uint8_t* krow = ks + key * (D * 2);
-          f32x16 acc = (f32x16){};
-#pragma unroll
-          for (int s = 0; s < C::NDS; ++s) {
-            const u32x4 kv = ld_lds16(krow + (k_swz<D>(key, 2 * s + g) << 4));
-            acc = mfma32(as_bf16x8(kv), qf[s], acc);
-          }
-          sacc[kb] = acc;
-        }
-
-        // ---- mask (only tiles that straddle the diagonal or the block end)
-        const bool full = (n0 + C::BN <= Sk) && (!a.causal || kvpos0 + n0 + C::BN - 1 <= qpos0 + r0);
-        if (!full) {
-          // visibility is monotone in the key, so this row sees exactly the
-          // tile-local keys [0, lim)
-          int64_t lim64 = (int64_t)Sk - n0;
-          if (a.causal) lim64 = min<int64_t>(lim64, qpos0 + row - kvpos0 - n0 + 1);
-          const int lim = (int)max<int64_t>(0, min<int64_t>(lim64, C::BN));
-#pragma unroll
-          for (int kb = 0; kb < C::NKB; ++kb) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int kl = kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-              sacc[kb][i] = (kl < lim) ? sacc[kb][i] : kNegInf;
-            }
-          }
-        }
-
-        // ---- online softmax (base 2), lazily rescaled
-        float mx = sacc[0][0];
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-        mx = fmaxf(mx, xor32(mx));
-        const float mt = mx * C::SCALE_LOG2;
-        if (__any(mt > m_run + kTau)) {
-          const float m_new = fmaxf(m_run, mt);
-          const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
-          l_run *= alpha;
-#pragma unroll
-          for (int db = 0; db < C::NDB; ++db) oacc[db] *= alpha;
-          m_run = m_new;
-        }
-        const float mref = (m_run == kNegInf) ? 0.f : m_run;
-
-        u32x4 pk[C::NKB][2];
-        float lsum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb) {
-          float p[16];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            p[i] = fast_exp2(fmaf(sacc[kb][i], C::SCALE_LOG2, -mref));
-            lsum += p[i];
-          }
-#pragma unroll
-          for (int t2 = 0; t2 < 2; ++t2)
-            pk[kb][t2] = (u32x4){pack_bf16(p[8 * t2 + 0], p[8 * t2 + 1]), pack_bf16(p[8 * t2 + 2], p[8 * t2 + 3]),
-                                 pack_bf16(p[8 * t2 + 4], p[8 * t2 + 5]), pack_bf16(p[8 * t2 + 6], p[8 * t2 + 7])};
-        }
-        l_run += lsum;
-
-        // ---- O^T += V^T P^T; k-slot j of lane group g <-> key
-        //      32 kb + 16 t2 + 8 (j / 4) + 4 g + (j % 4), matching the S^T layout
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-          const int d = db * 32 + l32;
-          const uint8_t* vrow = vs + d * C::VROW;
-          const int sw = v_swz(d);
-#pragma unroll
-          for (int kb = 0; kb < C::NKB; ++kb) {
-#pragma unroll
-            for (int t2 = 0; t2 < 2; ++t2) {
-              const int c8 = 8 * kb + 4 * t2 + g;
-              const u32x2 lo = ld_lds8(vrow + ((c8 ^ sw) << 3));
-              const u32x2 hi = ld_lds8(vrow + (((c8 + 2) ^ sw) << 3));
-              const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
-              oacc[db] = mfma32(as_bf16x8(av), as_bf16x8(pk[kb][t2]), oacc[db]);
-            }
-          }
-        }
-      }
-
-      if (has_next) store_tile((t + 1) & 1);
-      __syncthreads();
-    }
-  }
-
-  // ---- epilogue: combine the two half-rows' sums, normalise, store
-  const float l_tot = l_run + xor32(l_run);
-  if (row < a.Sq) {
-    const bool acc = a.accumulate != 0;
-    const RowOut ro = row_out(m_run, l_tot, acc, acc ? lp[(int64_t)row * a.l_ss] : 0.f);
-    float* orow = op + (int64_t)row * a.o_ss;
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db) {
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        float* dst = orow + db * 32 + 8 * i4 + 4 * g;
-        f32x4 v4 = {oacc[db][4 * i4 + 0] * ro.s_new, oacc[db][4 * i4 + 1] * ro.s_new, oacc[db][4 * i4 + 2] * ro.s_new,
-                    oacc[db][4 * i4 + 3] * ro.s_new};
-        if (acc) {
-          const f32x4 old = *reinterpret_cast<const f32x4*>(dst);
-          v4 = (f32x4){fmaf(old[0], ro.s_old, v4[0]), fmaf(old[1], ro.s_old, v4[1]), fmaf(old[2], ro.s_old, v4[2]),
-                       fmaf(old[3], ro.s_old, v4[3])};
-        }
-        *reinterpret_cast<f32x4*>(dst) = v4;
-      }
-    }
-    if (g == 0 && lp != nullptr) lp[(int64_t)row * a.l_ss] = ro.lse;
-  }
-}
-
+constexpr float kTwoTau = 256.0f;  // 2^8: the reference moves when a probability would exceed it
 
 // ---------------------------------------------------------------------------
-// D = 128 kernel.
+// The kernel, for head dimensions D = 128 and D = 64.
 //
 // Workgroup = 8 waves = 256 query rows of one head, 32 rows per wave (two
 // waves per SIMD).  K and V tiles of 64 keys go straight from global memory
@@ -310,12 +43,13 @@ __global__ __launch_bounds__(256) void partial_bf16_kernel(const PartialLaunch a
 // so when lane s addresses row key0 + s/4 at columns D0 + 4(s%4), lane i
 // receives V[key0 .. key0+3][D0 + i] -- four keys of one column.
 //
-// LDS: the K tiles of the three stages (64 keys x 256 B each, 16-byte chunks
-// XOR-swizzled by key & 15), then their V tiles (chunks XOR-swizzled by
-// 4 (key & 3)); with K and V apart, every operand read reaches its data
-// through the 16-bit offset of ds_read from one per-lane base.  The query
-// tile (256 rows x 256 B) has a 64 KB region of its own, filled once per
-// workgroup, for 160 KB in all.
+// LDS: the K tiles of the three stages (64 keys x 2D bytes each, 16-byte
+// chunks XOR-swizzled by key & 15 for D = 128, by (key >> 1) & 7 for the
+// 128-byte rows of D = 64), then their V tiles (chunks XOR-swizzled by
+// 4 (key & 3), or 2 (key & 3)); with K and V apart, every operand read
+// reaches its data through the 16-bit offset of ds_read from one per-lane
+// base.  The query tile has a region of its own (64 KB), filled once per
+// workgroup: 160 KB in all for D = 128, 112 KB for D = 64.
 //
 // Each wave's work is software-pipelined so that its matrix and vector work
 // overlap.  Iteration t runs two phases:
@@ -323,7 +57,8 @@ __global__ __launch_bounds__(256) void partial_bf16_kernel(const PartialLaunch a
 //      evaluates, packs and sums key block 1 of P(t);
 //   B: O^T += V(t)^T P(t)^T on the matrix cores, while the vector unit does
 //      key block 0 of P(t+1).
-// Each MFMA is followed by its slice of the vector work (one probability),
+// Each MFMA is followed by its slice of the vector work (one probability;
+// two with D = 64, whose phases have 8 MFMAs for the 16 probabilities),
 // skewed over three slots: slot j takes the exponential of score j, the
 // exponent argument of score j+1 and the row-sum add and bf16 pack of score
 // j-1, so no instruction of a slot waits on another of the same slot.  A
@@ -334,7 +69,7 @@ __global__ __launch_bounds__(256) void partial_bf16_kernel(const PartialLaunch a
 // The probabilities of a tile are evaluated against the running reference m
 // without first taking the tile's row max.  Once a tile's probabilities are
 // all in, a wave whose lanes all have a reference and partial sums of at
-// most 2^kTau (so every p <= 2^kTau) keeps them; any other wave recomputes
+// most 2^8 (so every p <= 2^8) keeps them; any other wave recomputes
 // that tile's scores (its K is still in LDS), moves the reference to the row
 // max and evaluates the probabilities again.  The move rescales the row sum
 // at once and O before the tile's PV.
@@ -370,10 +105,22 @@ __device__ __forceinline__ void pin(T& x) {
 // every chunk's partial goes to its own slot (item.slot + chunk): at each
 // boundary the finished partial is written and the softmax restarts exactly as
 // a launch of that chunk alone would.  Without SEG an item writes one result.
-template <bool SEG>
-__global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLaunch a, const int n_qtiles) {
-  constexpr int D = 128, BN = 64, NDS = 8, BM = 256;
-  constexpr int TBYTES = BN * D * 2;  // one K or V tile
+template <int D, bool SEG>
+__global__ __launch_bounds__(512) void partial_bf16_fast_kernel(const PartialLaunch a, const int n_qtiles) {
+  static_assert(D == 64 || D == 128, "head dimension 64 or 128");
+  constexpr int BN = 64, BM = 256;
+  constexpr int ROWB = D * 2;          // bytes of a Q, K or V row
+  constexpr int CH = D / 8;            // 16-byte chunks of a row
+  constexpr int NDS = D / 16;          // k-steps of S^T = K Q^T
+  constexpr int NDB = D / 32;          // 32-column blocks of O^T
+  constexpr int NQK = 2 * NDS;         // QK MFMAs of a tile (two key blocks)
+  constexpr int NPV = 4 * NDB;         // PV MFMAs of a tile (four 16-key groups)
+  // Each phase evaluates 16 probabilities per lane; with D = 64 a phase has 8
+  // MFMAs, so two probability slots follow each of them.
+  constexpr int RA = 16 / NQK, RB = 16 / NPV;
+  static_assert(16 % NQK == 0 && 16 % NPV == 0, "probability slots per MFMA");
+  constexpr int TBYTES = BN * ROWB;   // one K or V tile
+  constexpr int KB1 = 32 * ROWB;      // key block 1 of a K tile
   constexpr int NST = 3;              // LDS stages: tile t+2 is fetched while t and t+1 are read
   // LDS: the K tiles of all stages, then the V tiles, so every operand read's
   // offset from its per-lane base fits the 16-bit immediate of ds_read
@@ -381,10 +128,17 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
   constexpr int KLA = 4;              // K operand reads issued this many MFMAs ahead
   constexpr int VLA = 4;              // V operand reads issued this many MFMAs ahead
   constexpr int FW = 4;               // fetching waves
-  constexpr int FL = 1024 / (FW * 64);  // 16-byte pieces of K (and of V) per fetching lane
-  constexpr float SCALE_LOG2 = 0.12751743082459868f;  // log2(e) / sqrt(128)
+  constexpr int FL = BN * CH / (FW * 64);  // 16-byte pieces of K (and of V) per fetching lane
+  constexpr float SCALE_LOG2 = D == 64 ? 0.18033688011112042f : 0.12751743082459868f;  // log2(e) / sqrt(D)
+  // the query tile (rows of ROWB bytes); at least 64 KB, for the LSE copies of the merge tail
+  constexpr int QSM = BM * ROWB > 32 * 64 * 4 * 8 ? BM * ROWB : 32 * 64 * 4 * 8;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * NST * TBYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t qsm[BM * D * 2];  // the query tile, rows of 256 B
+  __shared__ __attribute__((aligned(16))) uint8_t qsm[QSM];
+  // Row swizzles of the 16-byte chunks in LDS: K (and Q) rows by the row (D = 128) or its
+  // half (D = 64, 128-byte rows), V rows by the row mod 4, so the operand reads of a
+  // 16-lane group spread over the banks.
+  auto kswz = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
+  auto vswz = [](int r) { return D == 128 ? 4 * (r & 3) : 2 * (r & 3); };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -425,16 +179,16 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
   if (a.causal) n_end = max(0, min(Sk, min(m0 + BM, a.Sq) - dpos));
   const int n_tiles = (n_end + BN - 1) / BN;
 
-  f32x16 o[4];
+  f32x16 o[NDB];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) o[db] = (f32x16){};
+  for (int db = 0; db < NDB; ++db) o[db] = (f32x16){};
   float m = kNegInf;  // running reference (log2 domain) of this lane's row
   float l = 0.f;      // this lane's share of the row sum, relative to m
 
   // With segments and a merge tail, the LSE of each segment's partial for this
-  // wave's rows is kept in LDS: 32 rows x 64 segments per wave, in the wave's
-  // own rows of the query tile area, which only this wave reads (once, in the
-  // prologue).
+  // wave's rows is kept in LDS: 32 rows x 64 segments per wave in the query tile
+  // area.  Every wave reads its query fragments in the prologue, before the
+  // first tile's barrier, and the first LSE copy is written after it.
   float* const seg_lse = reinterpret_cast<float*>(qsm) + wave * 32 * 64;
 
   // normalise and store this lane's row of segment `seg` (slot item.slot + seg)
@@ -447,7 +201,7 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
       const RowOut ro = row_out(m_, l_tot, acc, acc ? lps[(int64_t)row * a.l_ss] : 0.f);
       float* orow = op + seg * a.o_slot + (int64_t)row * a.o_ss;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           float* dst = orow + db * 32 + 8 * i4 + 4 * g;
@@ -469,16 +223,16 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
   if (n_tiles > 0) {
     bf16x8 qf[NDS];
     {
-      // The query tile reaches LDS by whole rows (16 lanes per 256-byte row, 16-byte
-      // chunks XOR-swizzled by the row), so each load moves four contiguous row
-      // pieces instead of 32 scattered ones; rows past the block end re-read its
-      // last row and are zeroed when read back.
+      // The query tile reaches LDS by whole rows (CH lanes per row, 16-byte chunks
+      // XOR-swizzled by the row), so each load moves contiguous row pieces
+      // instead of 32 scattered ones; rows past the block end re-read its last
+      // row and are zeroed when read back.
       const uint32_t qdst = lds_addr(qsm) + wave * 64 * 16;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < BM * CH / 512; ++i) {
         const int slot = i * 512 + wave * 64 + lane;
-        const int rr = slot >> 4;
-        const int c = (slot & 15) ^ (rr & 15);
+        const int rr = slot / CH;
+        const int c = (slot % CH) ^ kswz(rr);
         const int grow = min(m0 + rr, a.Sq - 1);
         gload_lds16(qp + (int64_t)grow * a.q_ss + c * 8, qdst + i * 512 * 16);
       }
@@ -486,29 +240,29 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
     // K operand of k-step s: row l32 (+32 for key block 1), chunk 2s+g swizzled by the row
     int koff[NDS];
 #pragma unroll
-    for (int s2 = 0; s2 < NDS; ++s2) koff[s2] = l32 * 256 + (((2 * s2 + g) ^ (l32 & 15)) << 4);
+    for (int s2 = 0; s2 < NDS; ++s2) koff[s2] = l32 * ROWB + (((2 * s2 + g) ^ kswz(l32)) << 4);
     // V^T operand, column block db: this lane addresses key 4g + ks (+16u + 8 half) at
-    // columns 32 db + 16 c16 + 4 (s & 3), chunk swizzled by 4 ks
-    int voff[4];
+    // columns 32 db + 16 c16 + 4 (s & 3), its chunk swizzled by the key mod 4
+    int voff[NDB];
     {
       const int s16 = lane & 15, ks = s16 >> 2, c16 = l32 >> 4, c8 = (s16 & 3) >> 1, bo = (s16 & 1) * 8;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) voff[db] = VBASE + (4 * g + ks) * 256 + ((4 * (db ^ ks) + 2 * c16 + c8) << 4) + bo;
+      for (int db = 0; db < NDB; ++db)
+        voff[db] = VBASE + (4 * g + ks) * ROWB + (((4 * db + 2 * c16 + c8) ^ vswz(ks)) << 4) + bo;
     }
     // Fetch: piece i of fetching wave fw, lane l is tile slot i*FW*64 + fw*64 + l,
-    // which holds key slot>>4 at physical chunk slot&15 (logical chunk for K:
-    // ^ (key & 15), for V: ^ 4 (key & 3)).  Each lane keeps its pieces' byte
-    // offsets from the tile start; the tile starts are scalar and advance one
-    // tile per fetch.
+    // which holds key slot/CH at physical chunk slot%CH (logical chunk: ^ kswz(key)
+    // for K, ^ vswz(key) for V).  Each lane keeps its pieces' byte offsets from
+    // the tile start; the tile starts are scalar and advance one tile per fetch.
     const bool fetcher = wave < FW;
     int fkey[FL];
     uint32_t kof[FL], vof[FL];
 #pragma unroll
     for (int i = 0; i < FL; ++i) {
       const int slot = i * FW * 64 + (wave % FW) * 64 + lane;
-      fkey[i] = slot >> 4;
-      kof[i] = (uint32_t)(2 * (fkey[i] * a.k_ss + (((slot & 15) ^ (fkey[i] & 15)) << 3)));
-      vof[i] = (uint32_t)(2 * (fkey[i] * a.v_ss + (((slot & 15) ^ (4 * (fkey[i] & 3))) << 3)));
+      fkey[i] = slot / CH;
+      kof[i] = (uint32_t)(2 * (fkey[i] * a.k_ss + (((slot % CH) ^ kswz(fkey[i])) << 3)));
+      vof[i] = (uint32_t)(2 * (fkey[i] * a.v_ss + (((slot % CH) ^ vswz(fkey[i])) << 3)));
     }
     const uint8_t* kt = reinterpret_cast<const uint8_t*>(kp);
     const uint8_t* vt = reinterpret_cast<const uint8_t*>(vp);
@@ -581,8 +335,8 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
       sc[0] = (f32x16){};
       sc[1] = (f32x16){};
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        sc[j & 1] = mfma32(as_bf16x8(ld_lds16(kbase + koff[j >> 1] + (j & 1) * 8192)), qf[j >> 1], sc[j & 1]);
+      for (int j = 0; j < NQK; ++j)
+        sc[j & 1] = mfma32(as_bf16x8(ld_lds16(kbase + koff[j >> 1] + (j & 1) * KB1)), qf[j >> 1], sc[j & 1]);
     };
     // move the reference to the row max of sc (never down)
     auto move_to_max = [&](const f32x16 (&sc)[2]) {
@@ -633,7 +387,7 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
         const bool ok = row < a.Sq;
 #pragma unroll
         for (int s2 = 0; s2 < NDS; ++s2)
-          qf[s2] = ok ? as_bf16x8(ld_lds16(qsm + rr * 256 + (((2 * s2 + g) ^ (rr & 15)) << 4))) : (bf16x8){};
+          qf[s2] = ok ? as_bf16x8(ld_lds16(qsm + rr * ROWB + (((2 * s2 + g) ^ kswz(rr)) << 4))) : (bf16x8){};
       }
       {
         scores(smem, snA);
@@ -666,17 +420,17 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
           if (pend) {
             write_out(seg_pend, m_pend, l_pend);
 #pragma unroll
-            for (int db = 0; db < 4; ++db) o[db] = (f32x16){};
+            for (int db = 0; db < NDB; ++db) o[db] = (f32x16){};
             pend = false;
           }
         }
 
-        u32x4 kop[16];
-        u32x2 vlo[16], vhi[16];
-        auto read_v = [&](int jj) {  // operands of PV MFMA jj: u = jj >> 2, db = jj & 3
-          const int u = jj >> 2, db = jj & 3;
-          vlo[jj] = ld_lds8_tr(cur + voff[db] + (16 * u) * 256);
-          vhi[jj] = ld_lds8_tr(cur + voff[db] + (16 * u + 8) * 256);
+        u32x4 kop[NQK];
+        u32x2 vlo[NPV], vhi[NPV];
+        auto read_v = [&](int jj) {  // operands of PV MFMA jj: key group u = jj / NDB, column block jj % NDB
+          const int u = jj / NDB, db = jj % NDB;
+          vlo[jj] = ld_lds8_tr(cur + voff[db] + (16 * u) * ROWB);
+          vhi[jj] = ld_lds8_tr(cur + voff[db] + (16 * u + 8) * ROWB);
         };
         // ---- phase A: S(t+1) = K(t+1) Q^T; key block 1 of P(t) ----
         __builtin_amdgcn_s_setprio(1);
@@ -684,16 +438,19 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
         x[0] = (f32x16){};
         x[1] = (f32x16){};
 #pragma unroll
-        for (int j = 0; j < KLA; ++j) kop[j] = ld_lds16(nxt + koff[j >> 1] + (j & 1) * 8192);
+        for (int j = 0; j < KLA; ++j) kop[j] = ld_lds16(nxt + koff[j >> 1] + (j & 1) * KB1);
         float pe = 0.f, pp = 0.f;
         float xa = fmaf(s1[0], SCALE_LOG2, -mref);
         pin(xa);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          if (j + KLA < 16) kop[j + KLA] = ld_lds16(nxt + koff[(j + KLA) >> 1] + ((j + KLA) & 1) * 8192);
-          if (j >= 16 - VLA) read_v(j - (16 - VLA));
-          x[j & 1] = mfma32(as_bf16x8(kop[j]), qf[j >> 1], x[j & 1]);
+          if (j % RA == 0) {
+            const int jm = j / RA;  // QK MFMA jm: key block jm & 1, k-step jm >> 1
+            if (jm + KLA < NQK) kop[jm + KLA] = ld_lds16(nxt + koff[(jm + KLA) >> 1] + ((jm + KLA) & 1) * KB1);
+            if (jm >= NQK - VLA) read_v(jm - (NQK - VLA));
+            x[jm & 1] = mfma32(as_bf16x8(kop[jm]), qf[jm >> 1], x[jm & 1]);
+          }
           // slot j: exponent of score j, argument of score j+1, sum and pack of score j-1
           const float pv = fast_exp2(xa);
           if (j < 15) xa = fmaf(s1[j + 1], SCALE_LOG2, -mref);
@@ -726,7 +483,7 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
         __builtin_amdgcn_s_setprio(0);
         if (__builtin_expect(need, 0)) {
 #pragma unroll
-          for (int db = 0; db < 4; ++db) o[db] *= alpha;
+          for (int db = 0; db < NDB; ++db) o[db] *= alpha;
           need = false;
         }
         xa = fmaf(x[0][0], SCALE_LOG2, -mref);
@@ -734,11 +491,14 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) {
-          if (jj + VLA < 16) read_v(jj + VLA);
-          const int u = jj >> 2, db = jj & 3;
-          const u32x4 av = {vlo[jj][0], vlo[jj][1], vhi[jj][0], vhi[jj][1]};
-          const u32x4 bp = {pw[4 * u], pw[4 * u + 1], pw[4 * u + 2], pw[4 * u + 3]};
-          o[db] = mfma32(as_bf16x8(av), as_bf16x8(bp), o[db]);
+          if (jj % RB == 0) {
+            const int jm = jj / RB;  // PV MFMA jm: key group u, column block db
+            if (jm + VLA < NPV) read_v(jm + VLA);
+            const int u = jm / NDB, db = jm % NDB;
+            const u32x4 av = {vlo[jm][0], vlo[jm][1], vhi[jm][0], vhi[jm][1]};
+            const u32x4 bp = {pw[4 * u], pw[4 * u + 1], pw[4 * u + 2], pw[4 * u + 3]};
+            o[db] = mfma32(as_bf16x8(av), as_bf16x8(bp), o[db]);
+          }
           const float pv = fast_exp2(xa);
           if (jj < 15) xa = fmaf(x[0][jj + 1], SCALE_LOG2, -mref);
           if (jj > 0) {
@@ -811,7 +571,7 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
     const int n_seg = (Sk + a.seg_tiles * BN - 1) / (a.seg_tiles * BN);
     if (last_seg + 1 < n_seg) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] = (f32x16){};
+      for (int db = 0; db < NDB; ++db) o[db] = (f32x16){};
       m = kNegInf;
       l = 0.f;
       for (int seg = last_seg + 1; seg < n_seg; ++seg) write_out(seg, m, l);
@@ -825,18 +585,19 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
       const bool pq = a.pass_q != 0;
       float M = kNegInf;
       for (int c = 0; c < n_seg; ++c) M = fmaxf(M, seg_lse[c * 32 + l32]);
-      f32x4 acc[16];
+      constexpr int NP = 4 * NDB;  // 16-byte pieces of this lane's row
+      f32x4 acc[NP];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) acc[k] = (f32x4){};
+      for (int k = 0; k < NP; ++k) acc[k] = (f32x4){};
       float den = 0.f;
       const float* const orow = op + (int64_t)row * a.o_ss + 4 * g;
-      auto load_seg = [&](int j, f32x4 (&v)[16]) {
+      auto load_seg = [&](int j, f32x4 (&v)[NP]) {
         const float* src = orow + j * a.o_slot;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) v[k] = *reinterpret_cast<const f32x4*>(src + (k >> 2) * 32 + 8 * (k & 3));
+        for (int k = 0; k < NP; ++k) v[k] = *reinterpret_cast<const f32x4*>(src + (k >> 2) * 32 + 8 * (k & 3));
       };
       if (M != kNegInf) {
-        f32x4 cur[16], nxt[16];
+        f32x4 cur[NP], nxt[NP];
         int j = arrival_kv(pq, i, n_seg, 0);
         load_seg(j, cur);
         for (int c = 0; c < n_seg; ++c) {
@@ -845,9 +606,9 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
           const float w = merge_weight(seg_lse[j * 32 + l32], M);
           den += w;
 #pragma unroll
-          for (int k = 0; k < 16; ++k) merge_acc(acc[k], w, cur[k]);
+          for (int k = 0; k < NP; ++k) merge_acc(acc[k], w, cur[k]);
 #pragma unroll
-          for (int k = 0; k < 16; ++k) cur[k] = nxt[k];
+          for (int k = 0; k < NP; ++k) cur[k] = nxt[k];
           j = jn;
         }
       }
@@ -855,7 +616,7 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
       const int64_t grow = (int64_t)i * a.chunk_len + row;
       const int64_t fo = b * a.f_sb + grow * a.f_ss + h * a.f_sh + 4 * g;
 #pragma unroll
-      for (int k = 0; k < 16; ++k)
+      for (int k = 0; k < NP; ++k)
         store_row(a.final_out, a.final_bf16 != 0, fo + (k >> 2) * 32 + 8 * (k & 3), acc[k] * inv);
       if (g == 0 && a.final_lse != nullptr) a.final_lse[b * a.fl_sb + grow * a.fl_ss + h * a.fl_sh] = merged_lse(M, den);
     }
@@ -864,18 +625,20 @@ __global__ __launch_bounds__(512) void partial_bf16_d128_kernel(const PartialLau
 
 }  // namespace
 
-int partial_bf16_rows_per_block(int D) { return D == 128 ? 256 : 128; }
+int partial_bf16_rows_per_block(int D) { return (D == 64 || D == 128) ? 256 : 128; }
 
 hipError_t launch_partial_bf16(const PartialLaunch& a, int D, int n_qtiles, hipStream_t s) {
   const long long blocks = (long long)a.n_items * a.B * a.Hq * n_qtiles;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (D == 128 && a.seg_tiles > 0)
-    hipLaunchKernelGGL(partial_bf16_d128_kernel<true>, dim3((unsigned)blocks), dim3(512), 0, s, a, n_qtiles);
+    hipLaunchKernelGGL((partial_bf16_fast_kernel<128, true>), dim3((unsigned)blocks), dim3(512), 0, s, a, n_qtiles);
   else if (D == 128)
-    hipLaunchKernelGGL(partial_bf16_d128_kernel<false>, dim3((unsigned)blocks), dim3(512), 0, s, a, n_qtiles);
+    hipLaunchKernelGGL((partial_bf16_fast_kernel<128, false>), dim3((unsigned)blocks), dim3(512), 0, s, a, n_qtiles);
+  else if (D == 64 && a.seg_tiles > 0)
+    hipLaunchKernelGGL((partial_bf16_fast_kernel<64, true>), dim3((unsigned)blocks), dim3(512), 0, s, a, n_qtiles);
   else if (D == 64)
-    hipLaunchKernelGGL(partial_bf16_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, s, a, n_qtiles);
+    hipLaunchKernelGGL((partial_bf16_fast_kernel<64, false>), dim3((unsigned)blocks), dim3(512), 0, s, a, n_qtiles);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -42,7 +42,7 @@ def _write_counters(d, rows):
 def test_counter_summary_scales_by_the_copy_kernel(tmp_path, monkeypatch):
     out = tmp_path / "traffic.txt"
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
-    k, copy = "partial_bf16_d128_kernel(args)", "vectorized_elementwise_kernel<MulFunctor>"
+    k, copy = "partial_bf16_fast_kernel<128, false>(args)", "vectorized_elementwise_kernel<MulFunctor>"
     gib_kib = (1 << 30) / 1024.0
     # the copy kernel's FETCH_SIZE reads half its true bytes (scale 2), WRITE_SIZE all of them
     _write_counters(tmp_path / "f", [(k, "FETCH_SIZE", 1000.0, 0, 1), (k, "FETCH_SIZE", 3000.0, 0, 1),
@@ -79,7 +79,7 @@ def test_trace_summary_and_its_readback(tmp_path, monkeypatch):
     with open(d / "kt_kernel_stats.csv", "w", newline="") as f:
         wr = csv.writer(f)
         wr.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"])
-        wr.writerow(["partial_bf16_d128_kernel<false>(args)", 96, 96 * 3.5e6, 3.5e6, 99.0, 1e6, 7e6, 1.0])
+        wr.writerow(["partial_bf16_fast_kernel<128, false>(args)", 96, 96 * 3.5e6, 3.5e6, 99.0, 1e6, 7e6, 1.0])
         wr.writerow(["decode_stream_kernel<128>(args)", 10, 3.3e6, 3.3e5, 1.0, 3e5, 4e5, 1.0])
     bj = tmp_path / "b.json"
     bj.write_text(json.dumps({"ms_per_step": 57.0, "value": 1234.5,
