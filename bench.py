@@ -476,8 +476,8 @@ def main(argv=None) -> int:
                 log(f"[bench] {w1.name} {name} rep {i + 1}/3: {ts[-1]:.1f} ms")
             res1[name] = tf(w1.flops(), sorted(ts)[1])
         result["prefill_1m"] = {"workload": w1.name, "order": "pass_kv", "flop": w1.flops(), **res1["ring_prefill"],
-                                "launch": "ring_prefill: one launch, each owner's query tiles walk their visible "
-                                "K/V chunks writing every pair's partial, then merge them in arrival order",
+                                "launch": "ring_prefill: every visible (Q chunk, K/V chunk) pair's partial in one "
+                                "launch (chunks this long go per pair), then the ring merge in arrival order",
                                 "fused": res1["fused"]}
         del x, o1, l1, ws1
         torch.cuda.empty_cache()

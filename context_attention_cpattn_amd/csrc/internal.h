@@ -40,7 +40,7 @@ struct PartialLaunch {
   int32_t causal;
   int32_t n_items;
   int32_t xcd_order;  // 1: each XCD takes a contiguous share of the grid; 0: launch order
-  int32_t accumulate; // 1: merge into the (O, LSE) already at the destination (lse not null)
+  int32_t accumulate; // 1: merge into the (O, LSE) already at the destination (lse not null; no segments)
   int32_t seg_tiles;  // > 0: an item's keys form segments of this many 64-key tiles, each one
                       // written as its own partial to slot item.slot + segment (D = 128 BF16)
   // With segments and final_out set, each query tile also merges its segments'

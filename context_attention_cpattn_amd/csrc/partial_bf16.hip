@@ -196,24 +196,30 @@ __global__ __launch_bounds__(512) void partial_bf16_fast_kernel(const PartialLau
   auto write_out = [&](int seg, float m_, float l_) {
     const float l_tot = pair32_sum(l_);
     if (row < a.Sq) {
-      const bool acc = a.accumulate != 0;
+      const bool acc = !SEG && a.accumulate != 0;  // chunk walks never accumulate
       float* const lps = lp != nullptr ? lp + seg * a.l_slot : nullptr;
-      const RowOut ro = row_out(m_, l_tot, acc, acc ? lps[(int64_t)row * a.l_ss] : 0.f);
-      float* orow = op + seg * a.o_slot + (int64_t)row * a.o_ss;
+      float* const orow = op + seg * a.o_slot + (int64_t)row * a.o_ss + 4 * g;
+      constexpr int NP = 4 * NDB;  // 16-byte pieces of this lane's half of the row
+      // An accumulating write reads the running row first, all of it before
+      // the first wait: one memory round trip instead of one per piece.
+      f32x4 old[NP];
+      float lse_old = 0.f;
+      if (acc) {
+        lse_old = lps[(int64_t)row * a.l_ss];
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+        for (int k = 0; k < NP; ++k) old[k] = *reinterpret_cast<const f32x4*>(orow + (k >> 2) * 32 + 8 * (k & 3));
+      }
+      const RowOut ro = row_out(m_, l_tot, acc, lse_old);
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          float* dst = orow + db * 32 + 8 * i4 + 4 * g;
-          f32x4 v4 = {o[db][4 * i4 + 0] * ro.s_new, o[db][4 * i4 + 1] * ro.s_new, o[db][4 * i4 + 2] * ro.s_new,
-                      o[db][4 * i4 + 3] * ro.s_new};
-          if (acc) {
-            const f32x4 old = *reinterpret_cast<const f32x4*>(dst);
-            v4 = (f32x4){fmaf(old[0], ro.s_old, v4[0]), fmaf(old[1], ro.s_old, v4[1]), fmaf(old[2], ro.s_old, v4[2]),
-                         fmaf(old[3], ro.s_old, v4[3])};
-          }
-          *reinterpret_cast<f32x4*>(dst) = v4;
-        }
+      for (int k = 0; k < NP; ++k) {
+        const int db = k >> 2, i4 = k & 3;
+        f32x4 v4 = {o[db][4 * i4 + 0] * ro.s_new, o[db][4 * i4 + 1] * ro.s_new, o[db][4 * i4 + 2] * ro.s_new,
+                    o[db][4 * i4 + 3] * ro.s_new};
+        if (acc)
+          v4 = (f32x4){fmaf(old[k][0], ro.s_old, v4[0]), fmaf(old[k][1], ro.s_old, v4[1]),
+                       fmaf(old[k][2], ro.s_old, v4[2]), fmaf(old[k][3], ro.s_old, v4[3])};
+        *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * i4) = v4;
+      }
       if (g == 0 && lps != nullptr) lps[(int64_t)row * a.l_ss] = ro.lse;
       if constexpr (SEG)
         if (g == 0 && a.final_out != nullptr) seg_lse[seg * 32 + l32] = ro.lse;
