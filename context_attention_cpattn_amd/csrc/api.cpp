@@ -120,9 +120,30 @@ cpattn::PartialLaunch base_partial(const cpattn_tensor& q, const cpattn_tensor& 
   return a;
 }
 
-hipError_t launch_partial(const cpattn::PartialLaunch& a, int dtype, int D, int Sq, hipStream_t st) {
+hipError_t launch_partial(cpattn::PartialLaunch& a, int dtype, int D, int Sq, hipStream_t st) {
   if (dtype == CPATTN_BF16) {
-    const int rpb = cpattn::partial_bf16_rows_per_block(D);
+    // Packing heads trades workgroups for busy waves.  Estimated time: rounds of
+    // workgroups over the compute units, times 1.64 when a SIMD holds two busy
+    // waves instead of one (two waves per SIMD reach ~0.50 of peak against ~0.41
+    // for one, so a workgroup with twice the rows takes ~1.64 times as long).
+    int n_cu = 0;
+    if (cpattn::cu_count(&n_cu) != hipSuccess) n_cu = 1;
+    const int rpb0 = cpattn::partial_bf16_rows_per_block(D);
+    const int hp_max = cpattn::partial_bf16_head_pack_log2(Sq, a.G);
+    int hpl = 0;
+    long long best = -1;
+    for (int l = 0; l <= hp_max; ++l) {
+      const int rpb = rpb0 >> l;
+      const long long wgs = (long long)a.n_items * a.B * (a.Hq >> l) * ((Sq + rpb - 1) / rpb);
+      const int busy = std::min(8, (1 << l) * ((std::min(Sq, rpb) + 31) / 32));  // waves with rows
+      const long long est = (wgs + n_cu - 1) / n_cu * (busy > 4 ? 164 : 100);
+      if (best < 0 || est < best) {
+        best = est;
+        hpl = l;
+      }
+    }
+    a.head_pack_log2 = hpl;
+    const int rpb = rpb0 >> hpl;
     return cpattn::launch_partial_bf16(a, D, (Sq + rpb - 1) / rpb, st);
   }
   const int rpb = cpattn::partial_f32_rows_per_block(D);

@@ -41,6 +41,7 @@ struct PartialLaunch {
   int32_t n_items;
   int32_t xcd_order;  // 1: each XCD takes a contiguous share of the grid; 0: launch order
   int32_t accumulate; // 1: merge into the (O, LSE) already at the destination (lse not null; no segments)
+  int32_t head_pack_log2;  // bf16 kernel: a workgroup takes 2^this heads of one K/V head (launcher sets it)
   int32_t seg_tiles;  // > 0: an item's keys form segments of this many 64-key tiles, each one
                       // written as its own partial to slot item.slot + segment (D = 128 BF16)
   // With segments and final_out set, each query tile also merges its segments'
@@ -136,6 +137,9 @@ constexpr size_t kScratchBytes = size_t(64) << 20;
 hipError_t scratch_address(void** out);
 
 int partial_bf16_rows_per_block(int D);  // query rows per workgroup of the bf16 kernel
+// log2 of the query heads a bf16 workgroup takes: 1, 2 or 3 when query blocks of
+// at most 128, 64 or 32 rows leave room and the heads of a K/V group allow it
+int partial_bf16_head_pack_log2(int Sq, int G);
 int partial_f32_rows_per_block(int D);
 
 }  // namespace cpattn

@@ -146,21 +146,30 @@ __global__ __launch_bounds__(512) void partial_bf16_fast_kernel(const PartialLau
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
-  const int bh = a.B * a.Hq;
+  // Head packing: the workgroup's 256 query rows are 2^hpl heads of the same K/V
+  // head, RPH = 256 >> hpl rows of each, so that query blocks of 128 rows or fewer
+  // still give every wave rows.  Wave w takes head h0 + w / WPH and rows
+  // (w % WPH) * 32 of that head's RPH.
+  const int hpl = a.head_pack_log2;
+  const int WPH = 8 >> hpl;   // waves per head
+  const int RPH = BM >> hpl;  // query rows per head
+  const int hb_n = a.Hq >> hpl;
+  const int bh = a.B * hb_n;
   const int per_item = bh * n_qtiles;
   const int L = (a.xcd_order ? xcd_logical_block(blockIdx.x, per_item * a.n_items) : (int)blockIdx.x);
   const int item = L / per_item;
   int rem = L - item * per_item;
   const int qt = n_qtiles - 1 - rem / bh;
   rem = rem % bh;
-  const int b = rem / a.Hq;
-  const int h = rem - b * a.Hq;
-  const int kvh = h / a.G;
+  const int b = rem / hb_n;
+  const int h0 = (rem - b * hb_n) << hpl;
+  const int h = h0 + wave / WPH;  // this wave's head
+  const int kvh = h0 / a.G;
   const Item it = a.items[item];
   const int Sk = it.sk > 0 ? it.sk : a.Sk;  // keys of this item's K/V block
 
-  const __bf16* qp = static_cast<const __bf16*>(a.q) + b * a.q_sb + h * a.q_sh +
-                     (int64_t)it.q_chunk * a.chunk_len * a.q_ss;
+  // the Q block without its head offset (the query tile's rows span 2^hpl heads)
+  const __bf16* qb = static_cast<const __bf16*>(a.q) + b * a.q_sb + (int64_t)it.q_chunk * a.chunk_len * a.q_ss;
   const __bf16* kp = static_cast<const __bf16*>(a.k) + b * a.k_sb + kvh * a.k_sh +
                      (int64_t)it.kv_chunk * a.kv_chunk_len * a.k_ss;
   const __bf16* vp = static_cast<const __bf16*>(a.v) + b * a.v_sb + kvh * a.v_sh +
@@ -171,12 +180,12 @@ __global__ __launch_bounds__(512) void partial_bf16_fast_kernel(const PartialLau
   const int64_t kvpos0 = a.kv_pos0 + (int64_t)it.kv_chunk * a.kv_chunk_len;
 
   const int dpos = (int)max<int64_t>(-(1 << 30), min<int64_t>(1 << 30, kvpos0 - qpos0));
-  const int m0 = qt * BM;
-  const int r0 = m0 + wave * 32;
+  const int m0 = qt * RPH;
+  const int r0 = m0 + (wave % WPH) * 32;
   const int row = r0 + l32;
 
   int n_end = Sk;
-  if (a.causal) n_end = max(0, min(Sk, min(m0 + BM, a.Sq) - dpos));
+  if (a.causal) n_end = max(0, min(Sk, min(m0 + RPH, a.Sq) - dpos));
   const int n_tiles = (n_end + BN - 1) / BN;
 
   f32x16 o[NDB];
@@ -232,15 +241,16 @@ __global__ __launch_bounds__(512) void partial_bf16_fast_kernel(const PartialLau
       // The query tile reaches LDS by whole rows (CH lanes per row, 16-byte chunks
       // XOR-swizzled by the row), so each load moves contiguous row pieces
       // instead of 32 scattered ones; rows past the block end re-read its last
-      // row and are zeroed when read back.
+      // row and are zeroed when read back.  Tile row rr is row m0 + rr % RPH of
+      // head h0 + rr / RPH.
       const uint32_t qdst = lds_addr(qsm) + wave * 64 * 16;
 #pragma unroll
       for (int i = 0; i < BM * CH / 512; ++i) {
         const int slot = i * 512 + wave * 64 + lane;
         const int rr = slot / CH;
         const int c = (slot % CH) ^ kswz(rr);
-        const int grow = min(m0 + rr, a.Sq - 1);
-        gload_lds16(qp + (int64_t)grow * a.q_ss + c * 8, qdst + i * 512 * 16);
+        const int grow = min(m0 + (rr & (RPH - 1)), a.Sq - 1);
+        gload_lds16(qb + (h0 + (rr >> (8 - hpl))) * a.q_sh + (int64_t)grow * a.q_ss + c * 8, qdst + i * 512 * 16);
       }
     }
     // K operand of k-step s: row l32 (+32 for key block 1), chunk 2s+g swizzled by the row
@@ -633,8 +643,14 @@ __global__ __launch_bounds__(512) void partial_bf16_fast_kernel(const PartialLau
 
 int partial_bf16_rows_per_block(int D) { return (D == 64 || D == 128) ? 256 : 128; }
 
+int partial_bf16_head_pack_log2(int Sq, int G) {
+  int hpl = 0;
+  while (hpl < 3 && Sq <= (256 >> (hpl + 1)) && G % (2 << hpl) == 0) ++hpl;
+  return hpl;
+}
+
 hipError_t launch_partial_bf16(const PartialLaunch& a, int D, int n_qtiles, hipStream_t s) {
-  const long long blocks = (long long)a.n_items * a.B * a.Hq * n_qtiles;
+  const long long blocks = (long long)a.n_items * a.B * (a.Hq >> a.head_pack_log2) * n_qtiles;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (D == 128 && a.seg_tiles > 0)
