@@ -178,9 +178,10 @@ cpattn_status cpattn_ring_select_order(const cpattn_tensor* q, const cpattn_tens
  * All ranks' partials of every step go out together (on one device the pairs
  * are independent), each into its workspace slot; then every Q chunk's
  * partials are merged in arrival order.  The result equals, bit for bit,
- * cpattn_ring_step for every step followed by cpattn_ring_merge (with K/V
- * chunks of a multiple of 64 tokens a query tile merges its own partials as
- * soon as its walk over its visible chunks has written them, with the same
+ * cpattn_ring_step for every step followed by cpattn_ring_merge (with BF16
+ * K/V chunks of a multiple of 64 tokens, at most 16384, and at least two
+ * owner query tiles per compute unit, a query tile walks its visible chunks
+ * and merges its own partials as soon as it has written them, with the same
  * arithmetic).
  *   q [B, Sq, Hq, D], k/v [B, Skv, Hkv, D]  BF16 or F32
  *   order              CPATTN_PASS_KV, CPATTN_PASS_Q or CPATTN_ORDER_AUTO

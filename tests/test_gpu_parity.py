@@ -161,8 +161,8 @@ def test_ring_small_orders(cp, P, order, causal):
 def test_ring_merge_follows_arrival_order(cp, P, order, causal, C):
     """The ring driver's merge equals, bit for bit, merging the same partials in the
     arrival order the oracle's schedule defines (partials via the partial entry point).
-    Chunks of a multiple of 64 tokens take the driver's one-walk-per-owner launch, whose
-    partials must be those of the per-pair launches bit for bit."""
+    These grids are small, so the driver launches per pair; its per-owner walk, whose
+    partials must be the same bits, is checked the same way in the chunk-walk tests."""
     H, D = 2, 128
     S = C * P
     q = draw(61 + P, (1, S, H, D), torch.bfloat16, 0).to(DEV)
@@ -180,22 +180,35 @@ def test_ring_merge_follows_arrival_order(cp, P, order, causal, C):
         assert torch.equal(lm, l[:, i * C:(i + 1) * C]), f"owner {i}: LSE differs"
 
 
-@pytest.mark.parametrize("P,C,B,Hkv,order,causal", [(64, 64, 1, 1, "pass_kv", True), (8, 64, 2, 2, "pass_q", False),
-                                                   (4, 320, 2, 2, "pass_kv", True), (3, 4096, 1, 1, "pass_q", True)])
-def test_ring_prefill_chunk_walk(cp, P, C, B, Hkv, order, causal):
-    """Chunks of a multiple of 64 tokens (up to 16384): the driver's per-owner walk that writes
-    every pair's partial at the chunk boundary and merges them at its end, against the oracle;
-    64-token chunks put a boundary after every tile, and 64 of them use every segment slot of the
-    merge tail."""
-    S, H = C * P, 4
-    q = draw(131 + P, (B, S, H, 128), torch.bfloat16, 0)
-    k = draw(131 + P, (B, S, Hkv, 128), torch.bfloat16, 1)
-    v = draw(131 + P, (B, S, Hkv, 128), torch.bfloat16, 2)
+@pytest.mark.parametrize("P,C,B,H,Hkv,D,order,causal", [(64, 64, 2, 4, 1, 128, "pass_kv", True),
+                                                        (8, 64, 2, 32, 2, 128, "pass_q", False),
+                                                        (4, 320, 2, 32, 2, 128, "pass_kv", True),
+                                                        (3, 4096, 1, 12, 1, 128, "pass_q", True),
+                                                        (4, 128, 4, 32, 2, 64, "pass_kv", True)])
+def test_ring_prefill_chunk_walk(cp, P, C, B, H, Hkv, D, order, causal):
+    """Chunks of a multiple of 64 tokens (up to 16384) on grids of at least two walking
+    workgroups per compute unit (on 256 of them): the driver's per-owner walk that writes every
+    pair's partial at the chunk boundary and merges them at its end, against the oracle and bit
+    for bit against the per-step launches and the merge; 64-token chunks put a boundary after
+    every tile, and 64 of them use every segment slot of the merge tail."""
+    S = C * P
+    walks = P * B * H * ((C + 255) // 256) >= 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    q = draw(131 + P, (B, S, H, D), torch.bfloat16, 0)
+    k = draw(131 + P, (B, S, Hkv, D), torch.bfloat16, 1)
+    v = draw(131 + P, (B, S, Hkv, D), torch.bfloat16, 2)
     o_ref, l_ref = oracle.full_attention(q, k, v, causal)
-    banner("ring chunk walk", P, C, B, Hkv, order, causal)
-    o, l = cp.ring_prefill(q.to(DEV), k.to(DEV), v.to(DEV), P, order, causal)
+    banner("ring chunk walk", P, C, B, H, Hkv, D, order, causal, "walks" if walks else "per pair on this device")
+    gq, gk, gv = q.to(DEV), k.to(DEV), v.to(DEV)
+    o, l = cp.ring_prefill(gq, gk, gv, P, order, causal)
     torch.cuda.synchronize()
-    compare(o, l, o_ref, l_ref, BF16_TOL, f"ring chunk walk P={P} C={C} B={B} Hkv={Hkv} {order} causal={causal}")
+    compare(o, l, o_ref, l_ref, BF16_TOL, f"ring chunk walk P={P} C={C} B={B} H={H} Hkv={Hkv} D={D} {order} causal={causal}")
+    ws = torch.empty(cp.ring_prefill_workspace_size(gq, P, causal), dtype=torch.uint8, device=DEV)
+    for step in range(P):
+        cp.ring_step(gq, gk, gv, P, step, ws, order, causal)
+    o_s, l_s = torch.empty_like(o), torch.empty_like(l)
+    cp.ring_merge(P, ws, o_s, l_s, order, causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o_s, o) and torch.equal(l_s, l), "ring steps + merge differ from the walk"
 
 
 @pytest.mark.parametrize("P,order,causal,D,dtype", [(1, "pass_kv", True, 128, "bf16"), (4, "pass_kv", True, 128, "bf16"),

@@ -2,8 +2,9 @@
 
 Each case draws a ring from a fixed stream: chunk count, Q and K/V chunk lengths
 (queries are the last Sq positions of the K/V sequence; K/V chunks a multiple
-of 64 tokens in most cases, so the per-owner chunk walk with its merge tail runs,
-ragged in the others), batch, query and K/V heads, head dimension, dtype, mask,
+of 64 tokens in most cases, so that the per-owner chunk walk with its merge tail
+runs wherever the grid has two walking workgroups per compute unit, ragged in the
+others), batch, query and K/V heads, head dimension, dtype, mask,
 ring order, output dtype, whether the LSE is wanted, and whether q, k and v are
 strided views of larger tensors.  For every case:
 
