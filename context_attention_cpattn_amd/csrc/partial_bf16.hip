@@ -32,8 +32,9 @@ constexpr float kTwoTau = 256.0f;  // 2^8: the reference moves when a probabilit
 // ---------------------------------------------------------------------------
 // The kernel, for head dimensions D = 128 and D = 64.
 //
-// Workgroup = 8 waves = 256 query rows of one head, 32 rows per wave (two
-// waves per SIMD).  K and V tiles of 64 keys go straight from global memory
+// Workgroup = 8 waves = 256 query rows of one head (or of 2, 4 or 8 heads of
+// one K/V head when query blocks are short), 32 rows per wave (two waves per
+// SIMD).  K and V tiles of 64 keys go straight from global memory
 // into LDS (global_load_lds_dwordx4), three stages deep; waves 0-3 do the
 // fetching, so the queue on the CU's memory unit stalls only the older wave
 // of each SIMD pair, which the pipeline below otherwise favours.  The V^T
