@@ -411,6 +411,30 @@ def test_workload_128k_owner_rows(cp, c4, owner, r0):
         compare(o[:, r0:r1], l[:, r0:r1], o_ref, l_ref, BF16_TOL, f"{w.name} {path} owner {owner} rows {r0}..{r1 - 1}")
 
 
+# The middle owners (1..14) at every row for two of the 16 heads, one owner per test: with the
+# owners 0 and 15 above, every query position of the sequence is compared with the oracle.
+C4_MID_HEADS = [0, 11]
+
+
+@pytest.mark.parametrize("owner", range(1, 15))
+def test_workload_128k_middle_owner_rows(cp, c4, owner):
+    import time
+
+    w, q, k, v, res = c4
+    r0, r1 = owner * 8192, (owner + 1) * 8192
+    hs = torch.as_tensor(C4_MID_HEADS)
+    t0 = time.perf_counter()
+    banner(w.name, f"oracle rows {r0}..{r1 - 1} (owner {owner}), heads {C4_MID_HEADS}")
+    o_ref, l_ref = oracle.partial_attention(q[:, r0:r1].index_select(2, hs).contiguous(), k[:, :r1], v[:, :r1], r0, 0,
+                                            True, row_block=256)
+    print(f"[oracle] {w.name} owner {owner}: {time.perf_counter() - t0:.1f} s", flush=True)
+    gh = hs.to(DEV)
+    for path in C4_PATHS:
+        o, l = res[path]
+        compare(o[:, r0:r1].index_select(2, gh), l[:, r0:r1].index_select(2, gh), o_ref, l_ref, BF16_TOL,
+                f"{w.name} {path} owner {owner} heads {C4_MID_HEADS}")
+
+
 @pytest.mark.timeout(900)
 def test_workload_1m_sampled(cp):
     w = si.WORKLOADS["prefill_bf16_s1m_p8"]
