@@ -446,5 +446,16 @@ def test_workload_1m_sampled(cp):
     torch.cuda.synchronize()
     banner(w.name, "oracle on sampled rows")
     _sampled_check(cp, w, o, l, q, k, v, w.name)
+    # and two blocks of 512 consecutive rows for two heads: across the boundary between chunks 3
+    # and 4, and the last rows of the sequence (each row at its full causal context)
+    hs = torch.as_tensor([0, 15])
+    gh = hs.to(DEV)
+    for r0 in (4 * w.chunk - 256, w.Sq - 512):
+        r1 = r0 + 512
+        banner(w.name, f"oracle rows {r0}..{r1 - 1}, heads 0 and 15")
+        o_ref, l_ref = oracle.partial_attention(q[:, r0:r1].index_select(2, hs).contiguous(), k[:, :r1], v[:, :r1],
+                                                r0, 0, True, row_block=256)
+        compare(o[:, r0:r1].index_select(2, gh), l[:, r0:r1].index_select(2, gh), o_ref, l_ref, BF16_TOL,
+                f"{w.name} rows {r0}..{r1 - 1}")
     del o, l, gq, gk, gv
     torch.cuda.empty_cache()
