@@ -9,7 +9,9 @@ per SIMD counted 1.64 times one with one) favours it.  The shapes below are
 sized so that 256 compute units pack them (the banner prints the packing the
 launcher picks on the present device), with ragged blocks and both head
 dimensions; the ring case also checks that its launches, packed or not,
-compute the same bits as the per-step launches and the merge.
+compute the same bits as the per-step launches and the merge.  Twelve seeded random
+calls (query block 2-128 rows, context up to 1200 keys, 2-16 query heads per K/V head,
+either head dimension, causal or not) add shapes no fixed case has.
 """
 import pytest
 import torch
@@ -122,3 +124,37 @@ def test_ring_head_packing(cp, case):
     of, lf = cp.ring_prefill_fused(gq, gk, gv, P, True)
     torch.cuda.synchronize()
     compare(of, lf, o_ref, l_ref, BF16_TOL, f"fused head packing {case}")
+
+
+N_RANDOM = 12
+
+
+def draw_packing_case(i: int) -> dict:
+    """A seeded random partial call whose grid is large enough to pack heads on 256 compute units."""
+    import numpy as np
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(entropy=9100, spawn_key=(i,))))
+    G = int(g.choice([2, 4, 8, 16]))
+    Hkv = int(g.choice([1, 2]))
+    Sq = int(g.integers(2, 129))
+    Skv = int(g.integers(Sq, 1200))
+    D = int(g.choice([64, 128]))
+    causal = bool(g.random() < 0.7)
+    q_off = int(g.integers(0, Skv - Sq + 1)) if causal else int(g.integers(0, 4096))
+    # enough sequences for 2048 unpacked workgroups: packing wins on 256 compute units
+    B = int(max(1, 2048 // (G * Hkv)))
+    return dict(B=B, Sq=Sq, Skv=Skv, Hq=G * Hkv, Hkv=Hkv, D=D, causal=causal, q_off=q_off)
+
+
+@pytest.mark.parametrize("i", range(N_RANDOM))
+def test_random_head_packing(cp, i):
+    c = draw_packing_case(i)
+    hpl = expected_pack(1, c["B"], c["Hq"], c["Hkv"], c["Sq"])
+    banner("random head packing", i, c, "heads per workgroup", 1 << hpl)
+    seed = 7500 + i
+    q = si.draw_tensor(seed, 0, (c["B"], c["Sq"], c["Hq"], c["D"]), torch.bfloat16)
+    k = si.draw_tensor(seed, 1, (c["B"], c["Skv"], c["Hkv"], c["D"]), torch.bfloat16)
+    v = si.draw_tensor(seed, 2, (c["B"], c["Skv"], c["Hkv"], c["D"]), torch.bfloat16)
+    o_ref, l_ref = oracle.partial_attention(q, k, v, c["q_off"], 0, c["causal"])
+    o, l = cp.partial(q.to(DEV), k.to(DEV), v.to(DEV), c["q_off"], 0, c["causal"])
+    torch.cuda.synchronize()
+    compare(o, l, o_ref, l_ref, BF16_TOL, f"random head packing {i}")
