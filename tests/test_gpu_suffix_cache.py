@@ -40,17 +40,21 @@ def suffix_reference(q, k, v, causal):
     return oracle.partial_attention(q, k, v, k.shape[1] - q.shape[1], 0, causal)
 
 
-# (B, Sq, Skv, P, Hq, Hkv, D, dtype): bf16 D = 128 with K/V chunks of a multiple of 64 keys (up to
-# 16384) takes the per-owner walk, the others one work item per pair
+# (B, Sq, Skv, P, Hq, Hkv, D, dtype): bf16 with K/V chunks of a multiple of 64 keys (up to 16384)
+# takes the per-owner walk when the owners' query tiles number at least two per compute unit (the
+# last three cases, on 256 of them; two of those also pack heads), the others one work item per pair
 SUFFIX_CASES = [
-    (1, 512, 2048, 4, 4, 1, 128, "bf16"),     # walk: 512-key chunks, 128-query chunks
-    (2, 300, 12480, 3, 4, 2, 128, "bf16"),    # walk: 4160-key chunks, ragged 100-query chunks
-    (1, 200, 4000, 4, 2, 1, 128, "bf16"),     # per pair: 1000-key chunks (not a multiple of 64)
+    (1, 512, 2048, 4, 4, 1, 128, "bf16"),     # 512-key chunks, 128-query chunks
+    (2, 300, 12480, 3, 4, 2, 128, "bf16"),    # 4160-key chunks, ragged 100-query chunks
+    (1, 200, 4000, 4, 2, 1, 128, "bf16"),     # 1000-key chunks (not a multiple of 64)
     (1, 1024, 1024, 8, 2, 1, 128, "bf16"),    # equal lengths through the same code
-    (1, 64, 8192, 16, 8, 1, 128, "bf16"),     # walk: 4 queries per chunk, 512-key chunks
+    (1, 64, 8192, 16, 8, 1, 128, "bf16"),     # 4 queries per chunk, 512-key chunks
     (2, 192, 960, 3, 4, 2, 64, "bf16"),       # D = 64
     (1, 128, 640, 2, 2, 1, 64, "f32"),        # fp32 vector path
     (1, 96, 1152, 3, 2, 2, 128, "f32"),
+    (8, 512, 2048, 4, 16, 1, 128, "bf16"),    # walk, 128-query chunks, two heads to a workgroup
+    (12, 300, 3840, 3, 16, 2, 128, "bf16"),   # walk, ragged 100-query chunks, 1280-key chunks
+    (8, 64, 8192, 16, 8, 1, 128, "bf16"),     # walk, 4 queries per chunk, four heads to a workgroup
 ]
 
 
