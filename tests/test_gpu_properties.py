@@ -201,3 +201,34 @@ def test_side_stream_buffers_survive_reuse(cp):
     compare(o, l, o_ref, l_ref, BF16_TOL, "ring_prefill on a side stream")
     compare(od, ld, od_ref, ld_ref, BF16_TOL, "splitkv_decode on a side stream")
     del junk
+
+
+def test_concurrent_streams_bit_identical(cp):
+    """Two different problems run at the same time on two streams, their ring steps interleaved,
+    give the same bits as each run alone: the library keeps no state between calls that two
+    streams could share (only the allocation-free decode's fixed scratch, which this does not use)."""
+    qa, ka, va = qkv(41, 4096, 8, 1, 128)          # 4 chunks of 1024: the chunk walk
+    qb, kb, vb = qkv(42, 2048, 16, 2, 64)          # 16 chunks of 128: per-pair launches (the whole ring packs heads)
+    def run(s1, s2):
+        ra = cp.ring_prefill(qa, ka, va, 4, "pass_kv", True, stream=s1)
+        oa = torch.full((1, 2048, 16, 64), float("nan"), device=DEV)
+        la = torch.full((1, 2048, 16), float("nan"), device=DEV)
+        s2.wait_stream(torch.cuda.current_stream())  # the fills above ran on the current stream
+        for step in range(16):
+            with torch.cuda.stream(s2):
+                cp.ring_step_accumulate(qb, kb, vb, 16, step, oa, la, "pass_q", True)
+        rf = cp.ring_prefill_fused(qa, ka, va, 4, True, stream=s1)
+        rb = cp.ring_prefill(qb, kb, vb, 16, "pass_q", True, stream=s2)
+        return ra, (oa, la), rf, rb
+    banner("concurrent streams", "alone")
+    alone = run(torch.cuda.current_stream(), torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    banner("concurrent streams", "together")
+    together = run(s1, s2)
+    s1.synchronize()
+    s2.synchronize()
+    torch.cuda.synchronize()
+    for name, x, y in zip(("ring prefill", "accumulating steps", "fused", "ring prefill (packed)"), alone, together):
+        assert torch.equal(x[0], y[0]) and torch.equal(x[1], y[1]), f"{name}: results differ between streams"
