@@ -45,6 +45,9 @@
  *    execution errors surface at the caller's next synchronisation.
  *  - Results are deterministic: no atomics on any accumulation path, and a
  *    fixed reduction order, so repeated calls give bitwise-identical output.
+ *  - Graph capture: a call enqueues kernel launches only (no allocation, copy
+ *    or memset on the stream), so calls may be recorded into a HIP graph; a
+ *    replay reuses the buffers and sizes of the recorded call.
  */
 #ifndef CPATTN_H
 #define CPATTN_H

@@ -232,3 +232,54 @@ def test_concurrent_streams_bit_identical(cp):
     torch.cuda.synchronize()
     for name, x, y in zip(("ring prefill", "accumulating steps", "fused", "ring prefill (packed)"), alone, together):
         assert torch.equal(x[0], y[0]) and torch.equal(x[1], y[1]), f"{name}: results differ between streams"
+
+
+def test_graph_capture_replays(cp):
+    """The ring entry points and the allocation-free decode, given their buffers, issue only kernel
+    launches on the caller's stream, so a caller can capture them in a HIP graph: the 4 accumulating
+    ring steps, a Pass-Q ring prefill, the fused prefill and a decode, captured once and replayed
+    three times with eager work between the replays, give the eager bits every time."""
+    P = 4
+    q, k, v = qkv(51, 4096, 8, 1, 128)
+    qd = si.draw_tensor(52, 0, (8, 1, 16, 128), torch.bfloat16).to(DEV)
+    kd = si.draw_tensor(52, 1, (8, 4096, 1, 128), torch.bfloat16).to(DEV)
+    vd = si.draw_tensor(52, 2, (8, 4096, 1, 128), torch.bfloat16).to(DEV)
+    bufs = {name: (torch.empty(1, 4096, 8, 128, device=DEV), torch.empty(1, 4096, 8, device=DEV))
+            for name in ("acc", "ring", "fused")}
+    dec = (torch.empty(8, 1, 16, 128, device=DEV), torch.empty(8, 1, 16, device=DEV))
+    ws = torch.empty(cp.ring_prefill_workspace_size(q, P, True), dtype=torch.uint8, device=DEV)
+
+    def work():
+        for step in range(P):
+            cp.ring_step_accumulate(q, k, v, P, step, *bufs["acc"], "pass_kv", True)
+        cp.ring_prefill(q, k, v, P, "pass_q", True, out=bufs["ring"][0], lse=bufs["ring"][1], workspace=ws)
+        cp.ring_prefill_fused(q, k, v, P, True, out=bufs["fused"][0], lse=bufs["fused"][1])
+        cp.splitkv_decode_noalloc(qd, kd, vd, 8, *dec)
+
+    banner("graph capture", "eager")
+    work()
+    torch.cuda.synchronize()
+    ref = {name: (o.clone(), l.clone()) for name, (o, l) in bufs.items()}
+    ref["decode"] = (dec[0].clone(), dec[1].clone())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        work()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    banner("graph capture", "capture")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    torch.cuda.synchronize()
+    outs = dict(bufs, decode=dec)
+    for rep in range(3):
+        for o, l in outs.values():  # eager work between the replays
+            o.fill_(float("nan"))
+            l.fill_(float("nan"))
+        torch.cuda.synchronize()
+        banner("graph capture", "replay", rep)
+        g.replay()
+        torch.cuda.synchronize()
+        for name, (o, l) in outs.items():
+            assert torch.equal(o, ref[name][0]) and torch.equal(l, ref[name][1]), f"replay {rep}: {name} differs"
