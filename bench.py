@@ -44,6 +44,8 @@ DECODE = "decode_b128_kv32k_p8"
 KERNEL_SRC = os.path.join(ROOT, "context_attention_cpattn_amd", "csrc", "partial_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "partial_bf16_prefill_s128k_p16_traffic.txt")
 TRACE_FILE = os.path.join(ROOT, "profiles", "partial_bf16_prefill_s128k_p16_trace.txt")
+DECODE_FILE = os.path.join(ROOT, "profiles", "decode_stream_b128_kv32k_p8.txt")
+DECODE_PROFILE_CMD = "python $R/bench.py --decode-only"
 PROFILE_CMD = "python bench.py --headline-only --no-cpu-baseline"
 COPY_BYTES = 1 << 30
 
@@ -194,6 +196,44 @@ def timed_reps(torch, stream, fn, reps: int, warm_ms: float = 50.0):
     return sorted(e[0].elapsed_time(e[1]) for e in ev)[reps // 2]
 
 
+def decode_bytes(wd) -> dict:
+    """Algorithmic HBM bytes of the split-KV decode of workload wd: the kernel reads K, V and Q and
+    writes every chunk's partial (O and LSE); the merge reads the partials and writes O and LSE."""
+    kv = 2 * wd.B * wd.Skv * wd.Hkv * wd.D * 2
+    qb = wd.B * wd.Hq * wd.D * 2
+    part = wd.n_chunks * wd.B * wd.Hq * (wd.D + 1) * 4
+    outb = wd.B * wd.Hq * (wd.D + 1) * 4
+    return {"kernel": kv + qb + part, "merge": part + outb, "total": kv + qb + 2 * part + outb}
+
+
+def gbs(nbytes: float, ms: float) -> dict:
+    g = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "GB/s": round(g, 1), "frac_hbm": round(g / PEAK_HBM_GBS, 4)}
+
+
+def time_decode(torch, cp, si, dev, stream, reps: int) -> dict:
+    """The split-KV decode of the decode workload (kernel + merge) and its allocation-free form."""
+    wd = si.WORKLOADS[DECODE]
+    log(f"[bench] drawing {wd.name} inputs")
+    dq, dk, dv = [t.to(dev) for t in si.make_qkv(wd)]
+    dws = torch.empty(cp.splitkv_decode_workspace_size(dq, dk, wd.n_chunks), dtype=torch.uint8, device=dev)
+    dout = torch.empty(wd.q_shape(), dtype=torch.float32, device=dev)
+    dlse = torch.empty(wd.q_shape()[:3], dtype=torch.float32, device=dev)
+    ms_d = timed_reps(torch, stream, lambda: cp.splitkv_decode(dq, dk, dv, wd.n_chunks, out=dout, lse=dlse,
+                                                               workspace=dws), reps, warm_ms=60.0)
+    ms_dn = timed_reps(torch, stream, lambda: cp.splitkv_decode_noalloc(dq, dk, dv, wd.n_chunks, dout, dlse), reps)
+    nb = decode_bytes(wd)["total"]
+    log(f"[bench] decode {ms_d:.3f} ms, no-alloc {ms_dn:.3f} ms")
+    return {"wd": wd, "tensors": (dq, dk, dv, dout, dlse), "ms": ms_d, "ms_noalloc": ms_dn,
+            "result": {"workload": wd.name, **gbs(nb, ms_d), "algorithmic_bytes": nb, "peak_GB/s": PEAK_HBM_GBS,
+                       "noalloc": gbs(nb, ms_dn)}}
+
+
+def decode_profile_values() -> dict:
+    """Entries of the committed decode profile summary of the current kernel sources."""
+    return _summary_values(DECODE_FILE, keep_text=("machine_host", "machine_gpu_uuid"))
+
+
 def tf(flops: float, ms: float) -> dict:
     t = flops / (ms * 1e-3) / 1e12
     return {"ms": round(ms, 4), "TFLOP/s": round(t, 2), "pct_bf16_peak": round(100 * t / PEAK_BF16_TFLOPS, 2)}
@@ -210,6 +250,11 @@ def main(argv=None) -> int:
                     help="only the timed Pass-KV ring steps (profiling runs: every partial-kernel launch is then a "
                          "headline ring step)")
     ap.add_argument("--no-1m", action="store_true", help="skip the 1M-token workload leg (~1 minute)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the split-KV decode workload, --steps timed calls (decode profiling runs)")
+    ap.add_argument("--summarize-decode", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "BENCH_JSON"),
+                    help="kernel trace and HBM traffic of the decode kernel and its merge, beside a plain "
+                         "--decode-only line of the same machine")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB fp32 copy kernel (counter calibration under rocprofv3 --pmc)")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
@@ -225,6 +270,8 @@ def main(argv=None) -> int:
         return summarize_pmc(*args.summarize_pmc)
     if args.summarize_trace:
         return summarize_trace(*args.summarize_trace)
+    if args.summarize_decode:
+        return summarize_decode(*args.summarize_decode)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
               "the simulated CP ranks all run on one device.", file=sys.stderr)
@@ -238,6 +285,15 @@ def main(argv=None) -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     machine = machine_id(torch)
+    if args.decode_only:
+        # profiling runs of the decode workload alone: every decode kernel and merge launch is a C3 decode
+        dec = time_decode(torch, cp, si, dev, torch.cuda.current_stream(dev), max(1, args.steps))
+        line = {"decode": dec["result"], "machine": machine, "reps": max(1, args.steps)}
+        if args.calibrate_copy:
+            _copy_calibration(torch, dev)
+            line["copy_calibration_bytes"] = COPY_BYTES
+        print(json.dumps(line), flush=True)
+        return 0
     w = si.WORKLOADS[PREFILL]
     log(f"[bench] {machine['device']} on {machine['host']}, {cp.version()}; drawing {w.name} inputs")
     q, k, v = si.make_qkv(w)
@@ -407,33 +463,20 @@ def main(argv=None) -> int:
     del qs, ks, vs, os_, ls_
 
     # ---- split-KV decode, its allocation-free form, decode over CP cache shards, and the cache write
-    wd = si.WORKLOADS[DECODE]
-    log(f"[bench] drawing {wd.name} inputs")
-    dq, dk, dv = [t.to(dev) for t in si.make_qkv(wd)]
-    dws = torch.empty(cp.splitkv_decode_workspace_size(dq, dk, wd.n_chunks), dtype=torch.uint8, device=dev)
-    dout = torch.empty(wd.q_shape(), dtype=torch.float32, device=dev)
-    dlse = torch.empty(wd.q_shape()[:3], dtype=torch.float32, device=dev)
     dreps = max(20, args.steps)
-    ms_d = timed_reps(torch, stream, lambda: cp.splitkv_decode(dq, dk, dv, wd.n_chunks, out=dout, lse=dlse,
-                                                               workspace=dws), dreps, warm_ms=60.0)
-    ms_dn = timed_reps(torch, stream, lambda: cp.splitkv_decode_noalloc(dq, dk, dv, wd.n_chunks, dout, dlse), dreps)
+    dec = time_decode(torch, cp, si, dev, stream, dreps)
+    wd = dec["wd"]
+    dq, dk, dv, dout, dlse = dec["tensors"]
+    result["decode"] = dec["result"]
+    prof = decode_profile_values()
+    if prof:
+        # the committed kernel trace and counters of the same kernel sources (another run, named machine)
+        result["decode"]["profiled"] = {k_: prof.get(k_) for k_ in (
+            "decode_kernel_avg_ms", "merge_kernel_avg_ms", "kernel_and_merge_GB/s", "frac_hbm_profiled",
+            "decode_kernel_hbm_bytes", "merge_kernel_hbm_bytes", "machine_gpu_uuid")}
+        result["decode"]["profiled"]["source"] = "profiles/decode_stream_b128_kv32k_p8.txt"
     kv_bytes = 2 * wd.B * wd.Skv * wd.Hkv * wd.D * 2
-    q_bytes = wd.B * wd.Hq * wd.D * 2
-    part_bytes = wd.n_chunks * wd.B * wd.Hq * (wd.D + 1) * 4
-    out_bytes = wd.B * wd.Hq * (wd.D + 1) * 4
-    dec_bytes = kv_bytes + q_bytes + 2 * part_bytes + out_bytes
-
-    def gbs(nbytes, ms):
-        g = nbytes / (ms * 1e-3) / 1e9
-        return {"ms": round(ms, 4), "GB/s": round(g, 1), "frac_hbm": round(g / PEAK_HBM_GBS, 4)}
-
-    result["decode"] = {"workload": wd.name, **gbs(dec_bytes, ms_d), "algorithmic_bytes": dec_bytes,
-                        "peak_GB/s": PEAK_HBM_GBS, "noalloc": gbs(dec_bytes, ms_dn)}
-    pmc = pmc_values()
-    if "decode_fetch_bytes_per_launch" in pmc and "decode_write_bytes_per_launch" in pmc:
-        result["decode"]["kernel_traffic_profiled"] = pmc["decode_fetch_bytes_per_launch"] + \
-            pmc["decode_write_bytes_per_launch"]
-    log(f"[bench] decode {ms_d:.3f} ms, no-alloc {ms_dn:.3f} ms")
+    dec_bytes = decode_bytes(wd)["total"]
     # the same cache as the KV shards of 8 CP ranks, each with room for 64 more tokens
     C = wd.Skv // wd.n_chunks
     ks8 = [torch.empty(wd.B, C + 64, wd.Hkv, wd.D, dtype=torch.bfloat16, device=dev) for _ in range(wd.n_chunks)]
@@ -448,7 +491,7 @@ def main(argv=None) -> int:
     result["cp_decode"] = {"what": f"{wd.name} new tokens against the {wd.n_chunks} shards",
                            **gbs(dec_bytes, ms_cd), "algorithmic_bytes": dec_bytes}
     log(f"[bench] cache write {ms_w8:.3f} ms, decode over shards {ms_cd:.3f} ms")
-    del dq, dk, dv, dws, dout, dlse, ks8, vs8, cws
+    del dec, dq, dk, dv, dout, dlse, ks8, vs8, cws
     torch.cuda.empty_cache()
 
     # ---- the 1M-token workload (Pass-KV ring with per-pair partials and merge, and the fused walk)
@@ -628,6 +671,93 @@ def summarize_pmc(fetch_dir: str, write_dir: str, clock_dir: str | None = None, 
             f.write(f"lds_bank_conflict_cycles_per_lds_active_cycle: "
                     f"{tot['SQ_LDS_BANK_CONFLICT'] / tot['SQ_LDS_IDX_ACTIVE']:.3f}\n")
     print(open(TRAFFIC_FILE).read())
+    return 0
+
+
+def _trace_stats(trace_dir: str) -> dict:
+    stats = {}
+    for path in glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True):
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                stats[r["Name"]] = (int(r["Calls"]), float(r["AverageNs"]) / 1e6)
+    if not stats:
+        raise SystemExit(f"no *kernel_stats.csv under {trace_dir}")
+    return stats
+
+
+def summarize_decode(trace_dir: str, fetch_dir: str, write_dir: str, bench_json: str) -> int:
+    """Kernel trace and HBM traffic of the split-KV decode (decode_stream_kernel and the merge_kernel
+    that follows it) from ``--decode-only`` runs under rocprofv3, beside the plain ``--decode-only``
+    line of the same run."""
+    import seeded_inputs as si
+    wd = si.WORKLOADS[DECODE]
+    nb = decode_bytes(wd)
+    stats = _trace_stats(trace_dir)
+
+    def find(part, avoid=None):
+        hits = [(n, v) for n, v in stats.items() if part in n and (avoid is None or avoid not in n)]
+        if len(hits) != 1:
+            raise SystemExit(f"expected one kernel matching {part!r} in the trace, found {[h[0] for h in hits]}")
+        return hits[0][1]
+
+    (kc, kms), (mc, mms) = find("decode_stream_kernel"), find("merge_kernel", avoid="ring_merge")
+    fr, wr = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
+    f_c, _ = _per_dispatch(fr, "FETCH_SIZE", "MulFunctor")
+    w_c, _ = _per_dispatch(wr, "WRITE_SIZE", "MulFunctor")
+    if None in (f_c, w_c):
+        raise SystemExit("missing counters for the copy kernel (run with --calibrate-copy)")
+    f_scale, w_scale = COPY_BYTES / (f_c * 1024.0), COPY_BYTES / (w_c * 1024.0)
+    traffic = {}
+    for label, part, avoid in (("decode_kernel", "decode_stream_kernel", None), ("merge_kernel", "merge_kernel", "ring")):
+        fv = [float(r["Counter_Value"]) for r in fr if r.get("Counter_Name") == "FETCH_SIZE"
+              and part in r.get("Kernel_Name", "") and (avoid is None or avoid not in r.get("Kernel_Name", ""))]
+        wv = [float(r["Counter_Value"]) for r in wr if r.get("Counter_Name") == "WRITE_SIZE"
+              and part in r.get("Kernel_Name", "") and (avoid is None or avoid not in r.get("Kernel_Name", ""))]
+        if not fv or not wv:
+            raise SystemExit(f"missing FETCH_SIZE/WRITE_SIZE for {part}")
+        traffic[label] = (sum(fv) / len(fv) * 1024.0 * f_scale, sum(wv) / len(wv) * 1024.0 * w_scale, len(fv))
+    line = [ln for ln in open(bench_json).read().splitlines() if ln.startswith("{")][-1]
+    b = json.loads(line)
+    both_ms = kms + mms
+    g = nb["total"] / (both_ms * 1e-3) / 1e9
+    with open(DECODE_FILE, "w") as f:
+        f.write(f"# Split-KV decode of {wd.name} (128 sequences x 1 new token, 16/1 heads, D = 128, 32768 cached\n")
+        f.write("# tokens in 8 chunks): decode_stream_kernel, then merge_kernel over the 8 partials.\n")
+        f.write("# On the MI355X machine, from /tmp with TMPDIR=/tmp, R = repository root, OUT = an output directory:\n")
+        f.write(f"#   {DECODE_PROFILE_CMD} --steps 20 > $OUT/decode_plain.json\n")
+        f.write(f"#   rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/dtrace -o kt -- {DECODE_PROFILE_CMD} --steps 20\n")
+        f.write(f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/dfetch -o p -- {DECODE_PROFILE_CMD} --steps 3 --calibrate-copy\n")
+        f.write(f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/dwrite -o p -- {DECODE_PROFILE_CMD} --steps 3 --calibrate-copy\n")
+        f.write("#   python $R/bench.py --summarize-decode $OUT/dtrace $OUT/dfetch $OUT/dwrite $OUT/decode_plain.json\n")
+        f.write(f"kernel_source_sha256_16: {kernel_hash()}\n")
+        f.write(f"machine_host: {b['machine']['host']}\n")
+        f.write(f"machine_gpu_uuid: {b['machine']['gpu_uuid']}\n")
+        f.write("# algorithmic bytes: K + V + Q read and the partials written by the kernel; partials read and\n")
+        f.write("# O + LSE written by the merge\n")
+        f.write(f"decode_kernel_algorithmic_bytes: {nb['kernel']}\n")
+        f.write(f"merge_kernel_algorithmic_bytes: {nb['merge']}\n")
+        f.write(f"# kernel trace (rocprofv3 --kernel-trace --stats): calls, average ms\n")
+        f.write(f"decode_kernel_calls: {kc}\n")
+        f.write(f"decode_kernel_avg_ms: {kms:.4f}\n")
+        f.write(f"merge_kernel_calls: {mc}\n")
+        f.write(f"merge_kernel_avg_ms: {mms:.4f}\n")
+        f.write(f"decode_kernel_GB/s: {nb['kernel'] / (kms * 1e-3) / 1e9:.1f}\n")
+        f.write(f"kernel_and_merge_GB/s: {g:.1f}\n")
+        f.write(f"frac_hbm_profiled: {g / PEAK_HBM_GBS:.4f}\n")
+        f.write("# HBM traffic per dispatch: FETCH_SIZE and WRITE_SIZE scaled by a 1 GiB copy kernel's readings\n")
+        f.write(f"copy_fetch_scale: {f_scale:.4f}\n")
+        f.write(f"copy_write_scale: {w_scale:.4f}\n")
+        for label in ("decode_kernel", "merge_kernel"):
+            fb, wb, n = traffic[label]
+            f.write(f"{label}_dispatches_counted: {n}\n")
+            f.write(f"{label}_fetch_bytes: {fb:.0f}\n")
+            f.write(f"{label}_write_bytes: {wb:.0f}\n")
+            f.write(f"{label}_hbm_bytes: {fb + wb:.0f}\n")
+        f.write("# the plain --decode-only line of the same call (HIP events, median of the timed calls)\n")
+        f.write(f"bench_decode_ms: {b['decode']['ms']}\n")
+        f.write(f"bench_decode_GB/s: {b['decode']['GB/s']}\n")
+        f.write(f"bench_decode_frac_hbm: {b['decode']['frac_hbm']}\n")
+    print(open(DECODE_FILE).read())
     return 0
 
 

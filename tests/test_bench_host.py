@@ -96,6 +96,47 @@ def test_trace_summary_and_its_readback(tmp_path, monkeypatch):
     assert bench.trace_values() == {}
 
 
+def test_decode_summary_and_its_readback(tmp_path, monkeypatch):
+    """The decode profile: trace averages of the decode kernel and of its merge (not the ring merge),
+    their bytes per dispatch scaled by the copy kernel, read back only for the same kernel sources."""
+    import json
+    out = tmp_path / "decode.txt"
+    monkeypatch.setattr(bench, "DECODE_FILE", str(out))
+    d = tmp_path / "tr"
+    d.mkdir()
+    dk, mk, rk = "decode_stream_kernel(cpattn::DecodeLaunch, int)", "merge_kernel(cpattn::MergeLaunch)", \
+        "ring_merge_kernel(cpattn::RingMergeLaunch)"
+    with open(d / "kt_kernel_stats.csv", "w", newline="") as f:
+        wr = csv.writer(f)
+        wr.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"])
+        wr.writerow([dk, 44, 44 * 3.0e5, 3.0e5, 90.0, 1e5, 4e5, 1.0])
+        wr.writerow([mk, 44, 44 * 1.0e4, 1.0e4, 5.0, 1e4, 2e4, 1.0])
+        wr.writerow([rk, 4, 4 * 9.0e5, 9.0e5, 5.0, 1e5, 1e6, 1.0])
+    copy = "vectorized_elementwise_kernel<MulFunctor>"
+    gib_kib = (1 << 30) / 1024.0
+    _write_counters(tmp_path / "f", [(dk, "FETCH_SIZE", 1000.0, 0, 1), (mk, "FETCH_SIZE", 10.0, 0, 1),
+                                     (rk, "FETCH_SIZE", 9999.0, 0, 1), (copy, "FETCH_SIZE", gib_kib / 2, 0, 1)])
+    _write_counters(tmp_path / "w", [(dk, "WRITE_SIZE", 40.0, 0, 1), (mk, "WRITE_SIZE", 4.0, 0, 1),
+                                     (rk, "WRITE_SIZE", 9999.0, 0, 1), (copy, "WRITE_SIZE", gib_kib, 0, 1)])
+    bj = tmp_path / "b.json"
+    bj.write_text("[bench] log line\n" + json.dumps({"decode": {"ms": 0.31, "GB/s": 6900.0, "frac_hbm": 0.8625},
+                                                     "machine": {"host": "hostB", "gpu_uuid": "u2"}}) + "\n")
+    assert bench.summarize_decode(str(d), str(tmp_path / "f"), str(tmp_path / "w"), str(bj)) == 0
+    nb = bench.decode_bytes(si.WORKLOADS[bench.DECODE])
+    assert nb["total"] == nb["kernel"] + nb["merge"]
+    assert nb["total"] == 2165972992  # 2 x 128 x 32768 x 128 x 2 B of K/V + Q + partials twice + O/LSE
+    pv = bench.decode_profile_values()
+    assert pv["machine_host"] == "hostB"
+    assert pv["decode_kernel_avg_ms"] == pytest.approx(0.3)
+    assert pv["merge_kernel_avg_ms"] == pytest.approx(0.01)
+    assert pv["kernel_and_merge_GB/s"] == pytest.approx(nb["total"] / 0.31e-3 / 1e9, abs=0.1)
+    assert pv["decode_kernel_fetch_bytes"] == pytest.approx(1000.0 * 1024 * 2.0)
+    assert pv["merge_kernel_hbm_bytes"] == pytest.approx(10.0 * 2048 + 4.0 * 1024)
+    assert pv["bench_decode_ms"] == pytest.approx(0.31)
+    out.write_text(out.read_text().replace(bench.kernel_hash(), "0" * 16))
+    assert bench.decode_profile_values() == {}
+
+
 def test_cpu_threads_respect_the_job_share(monkeypatch):
     n = len(os.sched_getaffinity(0))
     monkeypatch.setenv("OMP_NUM_THREADS", "1")
