@@ -46,6 +46,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "partial_bf16_prefill_s128k_p16_tr
 TRACE_FILE = os.path.join(ROOT, "profiles", "partial_bf16_prefill_s128k_p16_trace.txt")
 DECODE_FILE = os.path.join(ROOT, "profiles", "decode_stream_b128_kv32k_p8.txt")
 DECODE_PROFILE_CMD = "python $R/bench.py --decode-only"
+MERGE_FILE = os.path.join(ROOT, "profiles", "ring_merge_s128k_p16.txt")
+MERGE_PROFILE_CMD = "python $R/bench.py --merge-only"
 PROFILE_CMD = "python bench.py --headline-only --no-cpu-baseline"
 COPY_BYTES = 1 << 30
 
@@ -229,6 +231,18 @@ def time_decode(torch, cp, si, dev, stream, reps: int) -> dict:
                        "noalloc": gbs(nb, ms_dn)}}
 
 
+def ring_merge_bytes(w) -> int:
+    """Algorithmic HBM bytes of the ring merge of workload w (causal, every rank a chunk): each of the
+    P(P+1)/2 visible pairs' partial rows (O and LSE, fp32) read once, each owner's rows written once."""
+    P = w.n_chunks
+    return (P * (P + 1) // 2 + P) * w.chunk * w.Hq * w.B * 4 * (w.D + 1)
+
+
+def merge_profile_values() -> dict:
+    """Entries of the committed ring-merge profile summary of the current kernel sources."""
+    return _summary_values(MERGE_FILE, keep_text=("machine_host", "machine_gpu_uuid"))
+
+
 def decode_profile_values() -> dict:
     """Entries of the committed decode profile summary of the current kernel sources."""
     return _summary_values(DECODE_FILE, keep_text=("machine_host", "machine_gpu_uuid"))
@@ -252,6 +266,10 @@ def main(argv=None) -> int:
     ap.add_argument("--no-1m", action="store_true", help="skip the 1M-token workload leg (~1 minute)")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the split-KV decode workload, --steps timed calls (decode profiling runs)")
+    ap.add_argument("--merge-only", action="store_true",
+                    help="only the 128K ring's merge over its per-pair partials, --steps timed calls (profiling runs)")
+    ap.add_argument("--summarize-merge", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "BENCH_JSON"),
+                    help="kernel trace and HBM traffic of the ring merge, beside a plain --merge-only line")
     ap.add_argument("--summarize-decode", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "BENCH_JSON"),
                     help="kernel trace and HBM traffic of the decode kernel and its merge, beside a plain "
                          "--decode-only line of the same machine")
@@ -272,6 +290,8 @@ def main(argv=None) -> int:
         return summarize_trace(*args.summarize_trace)
     if args.summarize_decode:
         return summarize_decode(*args.summarize_decode)
+    if args.summarize_merge:
+        return summarize_merge(*args.summarize_merge)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
               "the simulated CP ranks all run on one device.", file=sys.stderr)
@@ -313,6 +333,23 @@ def main(argv=None) -> int:
             cp.ring_step_accumulate(gq, gk, gv, P, s, out, lse, order, True)
             if ev is not None:
                 ev[s][1].record(stream)
+
+    if args.merge_only:
+        # profiling runs of the ring merge alone: the 128K ring's per-pair partials once, then merges
+        ws = torch.empty(cp.ring_prefill_workspace_size(gq, P, True), dtype=torch.uint8, device=dev)
+        for s in range(P):
+            cp.ring_step(gq, gk, gv, P, s, ws, "pass_kv", True)
+        reps = max(1, args.steps)
+        ms_m = timed_reps(torch, stream, lambda: cp.ring_merge(P, ws, out, lse, "pass_kv", True), reps)
+        nb = ring_merge_bytes(w)
+        line = {"ring_merge": {"workload": w.name, **gbs(nb, ms_m), "algorithmic_bytes": nb,
+                               "peak_GB/s": PEAK_HBM_GBS}, "machine": machine, "reps": reps}
+        log(f"[bench] ring merge {ms_m:.3f} ms")
+        if args.calibrate_copy:
+            _copy_calibration(torch, dev)
+            line["copy_calibration_bytes"] = COPY_BYTES
+        print(json.dumps(line), flush=True)
+        return 0
 
     # ---- headline: the Pass-KV ring, one accumulating launch per ring step
     step_flops = ring_step_flops(w, "pass_kv")
@@ -398,14 +435,19 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         merge_ms.append(ev_m[0].elapsed_time(ev_m[1]))
     merge_ms = sorted(merge_ms)[1]
-    C, row_bytes = w.chunk, 4 * (w.D + 1)
-    n_parts = P * (P + 1) // 2
-    merge_bytes = (n_parts + P) * C * w.Hq * w.B * row_bytes
+    merge_bytes = ring_merge_bytes(w)
     result["ring_workspace"] = {**tf(total_flops, ms_w), "launch": "16 ring_step launches into per-pair workspace "
                                 "slots, then one ring_merge launch",
                                 "merge": {"ms": round(merge_ms, 4), "GB/s": round(merge_bytes / (merge_ms * 1e-3) / 1e9, 1),
                                           "frac_hbm": round(merge_bytes / (merge_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                                           "algorithmic_bytes": merge_bytes}}
+    mprof = merge_profile_values()
+    if mprof:
+        # the committed kernel trace and counters of the same kernel sources (another run, named machine)
+        result["ring_workspace"]["merge"]["profiled"] = {
+            "avg_ms": mprof.get("ring_merge_kernel_avg_ms"), "GB/s": mprof.get("ring_merge_GB/s"),
+            "frac_hbm": mprof.get("frac_hbm_profiled"), "hbm_bytes": mprof.get("ring_merge_kernel_hbm_bytes"),
+            "machine_gpu_uuid": mprof.get("machine_gpu_uuid"), "source": "profiles/ring_merge_s128k_p16.txt"}
     log(f"[bench] ring with workspace {ms_w:.2f} ms (merge {merge_ms:.3f} ms)")
 
     # ---- the whole ring as one call: per-owner walk, partials into the workspace, merged at the walk's end
@@ -685,6 +727,56 @@ def _trace_stats(trace_dir: str) -> dict:
     return stats
 
 
+def _kernel_profile(trace_dir: str, fetch_dir: str, write_dir: str, kernels) -> dict:
+    """Trace calls and average ms, and HBM bytes per dispatch (FETCH_SIZE and WRITE_SIZE scaled by a
+    1 GiB copy kernel's readings), of each kernel (label, name part, name part to avoid or None)."""
+    stats = _trace_stats(trace_dir)
+    fr, wr = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
+    f_c, _ = _per_dispatch(fr, "FETCH_SIZE", "MulFunctor")
+    w_c, _ = _per_dispatch(wr, "WRITE_SIZE", "MulFunctor")
+    if None in (f_c, w_c):
+        raise SystemExit("missing counters for the copy kernel (run with --calibrate-copy)")
+    out = {"copy_fetch_scale": COPY_BYTES / (f_c * 1024.0), "copy_write_scale": COPY_BYTES / (w_c * 1024.0)}
+
+    def match(name, part, avoid):
+        return part in name and (avoid is None or avoid not in name)
+
+    for label, part, avoid in kernels:
+        hits = [v for n, v in stats.items() if match(n, part, avoid)]
+        if len(hits) != 1:
+            raise SystemExit(f"expected one kernel matching {part!r} in the trace, found {len(hits)}")
+        fv = [float(r["Counter_Value"]) for r in fr
+              if r.get("Counter_Name") == "FETCH_SIZE" and match(r.get("Kernel_Name", ""), part, avoid)]
+        wv = [float(r["Counter_Value"]) for r in wr
+              if r.get("Counter_Name") == "WRITE_SIZE" and match(r.get("Kernel_Name", ""), part, avoid)]
+        if not fv or not wv:
+            raise SystemExit(f"missing FETCH_SIZE/WRITE_SIZE for {part}")
+        fb = sum(fv) / len(fv) * 1024.0 * out["copy_fetch_scale"]
+        wb = sum(wv) / len(wv) * 1024.0 * out["copy_write_scale"]
+        out[label] = {"calls": hits[0][0], "avg_ms": hits[0][1], "counted": len(fv), "fetch": fb, "write": wb}
+    return out
+
+
+def _write_kernel_lines(f, prof: dict, labels) -> None:
+    f.write("# kernel trace (rocprofv3 --kernel-trace --stats): calls, average ms\n")
+    for label in labels:
+        f.write(f"{label}_calls: {prof[label]['calls']}\n")
+        f.write(f"{label}_avg_ms: {prof[label]['avg_ms']:.4f}\n")
+    f.write("# HBM traffic per dispatch: FETCH_SIZE and WRITE_SIZE scaled by a 1 GiB copy kernel's readings\n")
+    f.write(f"copy_fetch_scale: {prof['copy_fetch_scale']:.4f}\n")
+    f.write(f"copy_write_scale: {prof['copy_write_scale']:.4f}\n")
+    for label in labels:
+        k = prof[label]
+        f.write(f"{label}_dispatches_counted: {k['counted']}\n")
+        f.write(f"{label}_fetch_bytes: {k['fetch']:.0f}\n")
+        f.write(f"{label}_write_bytes: {k['write']:.0f}\n")
+        f.write(f"{label}_hbm_bytes: {k['fetch'] + k['write']:.0f}\n")
+
+
+def _last_json(path: str) -> dict:
+    return json.loads([ln for ln in open(path).read().splitlines() if ln.startswith("{")][-1])
+
+
 def summarize_decode(trace_dir: str, fetch_dir: str, write_dir: str, bench_json: str) -> int:
     """Kernel trace and HBM traffic of the split-KV decode (decode_stream_kernel and the merge_kernel
     that follows it) from ``--decode-only`` runs under rocprofv3, beside the plain ``--decode-only``
@@ -692,34 +784,12 @@ def summarize_decode(trace_dir: str, fetch_dir: str, write_dir: str, bench_json:
     import seeded_inputs as si
     wd = si.WORKLOADS[DECODE]
     nb = decode_bytes(wd)
-    stats = _trace_stats(trace_dir)
-
-    def find(part, avoid=None):
-        hits = [(n, v) for n, v in stats.items() if part in n and (avoid is None or avoid not in n)]
-        if len(hits) != 1:
-            raise SystemExit(f"expected one kernel matching {part!r} in the trace, found {[h[0] for h in hits]}")
-        return hits[0][1]
-
-    (kc, kms), (mc, mms) = find("decode_stream_kernel"), find("merge_kernel", avoid="ring_merge")
-    fr, wr = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
-    f_c, _ = _per_dispatch(fr, "FETCH_SIZE", "MulFunctor")
-    w_c, _ = _per_dispatch(wr, "WRITE_SIZE", "MulFunctor")
-    if None in (f_c, w_c):
-        raise SystemExit("missing counters for the copy kernel (run with --calibrate-copy)")
-    f_scale, w_scale = COPY_BYTES / (f_c * 1024.0), COPY_BYTES / (w_c * 1024.0)
-    traffic = {}
-    for label, part, avoid in (("decode_kernel", "decode_stream_kernel", None), ("merge_kernel", "merge_kernel", "ring")):
-        fv = [float(r["Counter_Value"]) for r in fr if r.get("Counter_Name") == "FETCH_SIZE"
-              and part in r.get("Kernel_Name", "") and (avoid is None or avoid not in r.get("Kernel_Name", ""))]
-        wv = [float(r["Counter_Value"]) for r in wr if r.get("Counter_Name") == "WRITE_SIZE"
-              and part in r.get("Kernel_Name", "") and (avoid is None or avoid not in r.get("Kernel_Name", ""))]
-        if not fv or not wv:
-            raise SystemExit(f"missing FETCH_SIZE/WRITE_SIZE for {part}")
-        traffic[label] = (sum(fv) / len(fv) * 1024.0 * f_scale, sum(wv) / len(wv) * 1024.0 * w_scale, len(fv))
-    line = [ln for ln in open(bench_json).read().splitlines() if ln.startswith("{")][-1]
-    b = json.loads(line)
-    both_ms = kms + mms
-    g = nb["total"] / (both_ms * 1e-3) / 1e9
+    labels = ("decode_kernel", "merge_kernel")
+    prof = _kernel_profile(trace_dir, fetch_dir, write_dir, (("decode_kernel", "decode_stream_kernel", None),
+                                                             ("merge_kernel", "merge_kernel", "ring_merge")))
+    b = _last_json(bench_json)
+    kms, mms = prof["decode_kernel"]["avg_ms"], prof["merge_kernel"]["avg_ms"]
+    g = nb["total"] / ((kms + mms) * 1e-3) / 1e9
     with open(DECODE_FILE, "w") as f:
         f.write(f"# Split-KV decode of {wd.name} (128 sequences x 1 new token, 16/1 heads, D = 128, 32768 cached\n")
         f.write("# tokens in 8 chunks): decode_stream_kernel, then merge_kernel over the 8 partials.\n")
@@ -736,28 +806,53 @@ def summarize_decode(trace_dir: str, fetch_dir: str, write_dir: str, bench_json:
         f.write("# O + LSE written by the merge\n")
         f.write(f"decode_kernel_algorithmic_bytes: {nb['kernel']}\n")
         f.write(f"merge_kernel_algorithmic_bytes: {nb['merge']}\n")
-        f.write(f"# kernel trace (rocprofv3 --kernel-trace --stats): calls, average ms\n")
-        f.write(f"decode_kernel_calls: {kc}\n")
-        f.write(f"decode_kernel_avg_ms: {kms:.4f}\n")
-        f.write(f"merge_kernel_calls: {mc}\n")
-        f.write(f"merge_kernel_avg_ms: {mms:.4f}\n")
+        _write_kernel_lines(f, prof, labels)
+        f.write("# rates from the trace averages against the algorithmic bytes\n")
         f.write(f"decode_kernel_GB/s: {nb['kernel'] / (kms * 1e-3) / 1e9:.1f}\n")
         f.write(f"kernel_and_merge_GB/s: {g:.1f}\n")
         f.write(f"frac_hbm_profiled: {g / PEAK_HBM_GBS:.4f}\n")
-        f.write("# HBM traffic per dispatch: FETCH_SIZE and WRITE_SIZE scaled by a 1 GiB copy kernel's readings\n")
-        f.write(f"copy_fetch_scale: {f_scale:.4f}\n")
-        f.write(f"copy_write_scale: {w_scale:.4f}\n")
-        for label in ("decode_kernel", "merge_kernel"):
-            fb, wb, n = traffic[label]
-            f.write(f"{label}_dispatches_counted: {n}\n")
-            f.write(f"{label}_fetch_bytes: {fb:.0f}\n")
-            f.write(f"{label}_write_bytes: {wb:.0f}\n")
-            f.write(f"{label}_hbm_bytes: {fb + wb:.0f}\n")
         f.write("# the plain --decode-only line of the same call (HIP events, median of the timed calls)\n")
         f.write(f"bench_decode_ms: {b['decode']['ms']}\n")
         f.write(f"bench_decode_GB/s: {b['decode']['GB/s']}\n")
         f.write(f"bench_decode_frac_hbm: {b['decode']['frac_hbm']}\n")
     print(open(DECODE_FILE).read())
+    return 0
+
+
+def summarize_merge(trace_dir: str, fetch_dir: str, write_dir: str, bench_json: str) -> int:
+    """Kernel trace and HBM traffic of the ring merge of the 128K workload (ring_merge_kernel over the
+    136 per-pair partials of a Pass-KV ring) from ``--merge-only`` runs under rocprofv3, beside the
+    plain ``--merge-only`` line of the same run."""
+    import seeded_inputs as si
+    w = si.WORKLOADS[PREFILL]
+    nb = ring_merge_bytes(w)
+    prof = _kernel_profile(trace_dir, fetch_dir, write_dir, (("ring_merge_kernel", "ring_merge_kernel", None),))
+    b = _last_json(bench_json)
+    ms = prof["ring_merge_kernel"]["avg_ms"]
+    g = nb / (ms * 1e-3) / 1e9
+    with open(MERGE_FILE, "w") as f:
+        f.write(f"# Ring merge of {w.name}: ring_merge_kernel merging each of the 16 owners' partials\n")
+        f.write("# (136 per-pair slots of 8192 rows x 16 heads, fp32 O + LSE) in Pass-KV arrival order.\n")
+        f.write("# On the MI355X machine, from /tmp with TMPDIR=/tmp, R = repository root, OUT = an output directory:\n")
+        f.write(f"#   {MERGE_PROFILE_CMD} --steps 10 > $OUT/merge_plain.json\n")
+        f.write(f"#   rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/mtrace -o kt -- {MERGE_PROFILE_CMD} --steps 10\n")
+        f.write(f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/mfetch -o p -- {MERGE_PROFILE_CMD} --steps 3 --calibrate-copy\n")
+        f.write(f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/mwrite -o p -- {MERGE_PROFILE_CMD} --steps 3 --calibrate-copy\n")
+        f.write("#   python $R/bench.py --summarize-merge $OUT/mtrace $OUT/mfetch $OUT/mwrite $OUT/merge_plain.json\n")
+        f.write(f"kernel_source_sha256_16: {kernel_hash()}\n")
+        f.write(f"machine_host: {b['machine']['host']}\n")
+        f.write(f"machine_gpu_uuid: {b['machine']['gpu_uuid']}\n")
+        f.write("# algorithmic bytes: every slot's O and LSE read once, each owner's O and LSE written once\n")
+        f.write(f"ring_merge_kernel_algorithmic_bytes: {nb}\n")
+        _write_kernel_lines(f, prof, ("ring_merge_kernel",))
+        f.write("# rate from the trace average against the algorithmic bytes\n")
+        f.write(f"ring_merge_GB/s: {g:.1f}\n")
+        f.write(f"frac_hbm_profiled: {g / PEAK_HBM_GBS:.4f}\n")
+        f.write("# the plain --merge-only line of the same call (HIP events, median of the timed calls)\n")
+        f.write(f"bench_merge_ms: {b['ring_merge']['ms']}\n")
+        f.write(f"bench_merge_GB/s: {b['ring_merge']['GB/s']}\n")
+        f.write(f"bench_merge_frac_hbm: {b['ring_merge']['frac_hbm']}\n")
+    print(open(MERGE_FILE).read())
     return 0
 
 

@@ -137,6 +137,42 @@ def test_decode_summary_and_its_readback(tmp_path, monkeypatch):
     assert bench.decode_profile_values() == {}
 
 
+def test_merge_summary_and_its_readback(tmp_path, monkeypatch):
+    """The ring-merge profile: the trace average of ring_merge_kernel against the algorithmic bytes of
+    the 128K ring's 136 slots read and 16 owners written, and its counted traffic."""
+    import json
+    out = tmp_path / "merge.txt"
+    monkeypatch.setattr(bench, "MERGE_FILE", str(out))
+    d = tmp_path / "tr"
+    d.mkdir()
+    rk = "void cpattn::ring_merge_kernel<128>(cpattn::RingMergeLaunch)"
+    with open(d / "kt_kernel_stats.csv", "w", newline="") as f:
+        wr = csv.writer(f)
+        wr.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"])
+        wr.writerow([rk, 14, 14 * 1.9e6, 1.9e6, 40.0, 1.8e6, 2.0e6, 1.0])
+        wr.writerow(["partial_bf16_fast_kernel<128, false>(args)", 16, 16 * 3.5e6, 3.5e6, 60.0, 1e6, 7e6, 1.0])
+    copy = "vectorized_elementwise_kernel<MulFunctor>"
+    gib_kib = (1 << 30) / 1024.0
+    _write_counters(tmp_path / "f", [(rk, "FETCH_SIZE", 5000.0, 0, 1), (copy, "FETCH_SIZE", gib_kib / 2, 0, 1)])
+    _write_counters(tmp_path / "w", [(rk, "WRITE_SIZE", 600.0, 0, 1), (copy, "WRITE_SIZE", gib_kib, 0, 1)])
+    bj = tmp_path / "m.json"
+    bj.write_text(json.dumps({"ring_merge": {"ms": 1.88, "GB/s": 5470.0, "frac_hbm": 0.684},
+                              "machine": {"host": "hostC", "gpu_uuid": "u3"}}) + "\n")
+    assert bench.summarize_merge(str(d), str(tmp_path / "f"), str(tmp_path / "w"), str(bj)) == 0
+    w = si.WORKLOADS[bench.PREFILL]
+    nb = bench.ring_merge_bytes(w)
+    # 136 slots read + 16 owners written, 8192 rows x 16 heads x 129 floats each
+    assert nb == (136 + 16) * 8192 * 16 * 129 * 4
+    mv = bench.merge_profile_values()
+    assert mv["machine_host"] == "hostC"
+    assert mv["ring_merge_kernel_avg_ms"] == pytest.approx(1.9)
+    assert mv["ring_merge_GB/s"] == pytest.approx(nb / 1.9e-3 / 1e9, abs=0.1)
+    assert mv["ring_merge_kernel_hbm_bytes"] == pytest.approx(5000.0 * 2048 + 600.0 * 1024)
+    assert mv["bench_merge_ms"] == pytest.approx(1.88)
+    out.write_text(out.read_text().replace(bench.kernel_hash(), "0" * 16))
+    assert bench.merge_profile_values() == {}
+
+
 def test_cpu_threads_respect_the_job_share(monkeypatch):
     n = len(os.sched_getaffinity(0))
     monkeypatch.setenv("OMP_NUM_THREADS", "1")
