@@ -6,8 +6,8 @@ wider tensors and the outputs are views into wider buffers filled with NaN: the
 results must match the oracle, and nothing outside the views may change.  The
 shapes reach the chunk walk (enough walking workgroups for it on 256 compute
 units), the per-pair launches with the merge kernel (bf16 output), the
-accumulating ring steps, the fused prefill, the split-KV decode and the decode
-over cache shards.
+accumulating ring steps, the fused prefill, the split-KV decode, the decode
+over cache shards, and the cache write and append (bit-exact copies).
 """
 import pytest
 import torch
@@ -137,3 +137,32 @@ def test_cp_decode_strided_shards(cp):
     torch.cuda.synchronize()
     compare(o, l, o_ref, l_ref, BF16_TOL, "strided cp decode")
     guards_intact(ob, lb, H)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_kv_cache_write_strided(cp, dtype):
+    """K and V as head slices of differently shaped tensors (so their strides differ and they go in
+    launches of their own), written into shards that are head slices of wider NaN buffers; then one
+    appended token.  A copy: bit-exact against plain slicing, the head outside each view untouched."""
+    B, S, H, D, P, cap = 2, 2048, 3, 64, 4, 600
+    kb = si.draw_tensor(8106, 0, (B, S, H + 2, D), dtype).to(DEV)
+    vb = si.draw_tensor(8106, 1, (B, S, H + 1, D), dtype).to(DEV)
+    k, v = kb[:, :, 1:H + 1], vb[:, :, :H]
+    assert k.stride() != v.stride()
+    kbig = [torch.full((B, cap, H + 1, D), NAN, dtype=dtype, device=DEV) for _ in range(P)]
+    vbig = [torch.full((B, cap, H + 1, D), NAN, dtype=dtype, device=DEV) for _ in range(P)]
+    ks, vs = [t[:, :, 1:] for t in kbig], [t[:, :, :H] for t in vbig]
+    banner("strided cache write", dtype)
+    cp.kv_cache_write(k, v, P, ks, vs)
+    torch.cuda.synchronize()
+    C = S // P
+    for r in range(P):
+        assert torch.equal(ks[r][:, :C], k[:, r * C:(r + 1) * C]) and torch.equal(vs[r][:, :C], v[:, r * C:(r + 1) * C])
+        assert torch.isnan(ks[r][:, C:].float()).all() and torch.isnan(vs[r][:, C:].float()).all()
+        assert torch.isnan(kbig[r][:, :, 0].float()).all() and torch.isnan(vbig[r][:, :, H].float()).all()
+    new = si.draw_tensor(8107, 0, (B, 1, 2 * H, D), dtype).to(DEV)
+    banner("strided cache append", dtype)
+    cp.kv_cache_append(new[:, :, :H], new[:, :, H:], ks[1], vs[1], C)
+    torch.cuda.synchronize()
+    assert torch.equal(ks[1][:, C:C + 1], new[:, :, :H]) and torch.equal(vs[1][:, C:C + 1], new[:, :, H:])
+    assert torch.isnan(ks[1][:, C + 1:].float()).all() and torch.isnan(kbig[1][:, :, 0].float()).all()
