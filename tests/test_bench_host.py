@@ -173,6 +173,17 @@ def test_merge_summary_and_its_readback(tmp_path, monkeypatch):
     assert bench.merge_profile_values() == {}
 
 
+def test_committed_profiles_match_the_kernel_sources():
+    """Every committed profile summary was taken on the kernel sources as they stand: a change to a
+    kernel source without new profiles fails here (the bench would otherwise just drop the figures)."""
+    names = ["partial_bf16_prefill_s128k_p16_trace.txt", "partial_bf16_prefill_s128k_p16_traffic.txt",
+             "decode_stream_b128_kv32k_p8.txt", "ring_merge_s128k_p16.txt"]
+    for name in names:
+        path = os.path.join(bench.ROOT, "profiles", name)
+        tags = [ln.split(":", 1)[1].strip() for ln in open(path) if ln.startswith("kernel_source_sha256_16:")]
+        assert tags == [bench.kernel_hash()], f"{name} was taken on other kernel sources: {tags}"
+
+
 def test_cpu_threads_respect_the_job_share(monkeypatch):
     n = len(os.sched_getaffinity(0))
     monkeypatch.setenv("OMP_NUM_THREADS", "1")
