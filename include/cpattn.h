@@ -31,9 +31,10 @@
  *    or all F32 (fp32 vector arithmetic).  Partial outputs and LSE are F32.
  *    Sequence lengths below 2^30; B and H below 2^31; K and V token strides
  *    (stride_s) of at most 2^24 elements (CPATTN_ERR_UNSUPPORTED beyond).
- *  - Alignment: every data pointer 16-byte aligned; for Q/K/V/O the strides
- *    (stride_b, stride_s, stride_h) are multiples of 16 bytes' worth of
- *    elements (8 for BF16, 4 for F32).  LSE strides are unconstrained.
+ *  - Alignment: Q/K/V/O data pointers 16-byte aligned and their strides
+ *    (stride_b, stride_s, stride_h) multiples of 16 bytes' worth of elements
+ *    (8 for BF16, 4 for F32); LSE data pointers 4-byte aligned, LSE strides
+ *    unconstrained.  Workspaces 16-byte aligned.
  *  - Ownership: the caller owns every buffer and the stream.  The library
  *    allocates no device memory and keeps no pointer after a call returns;
  *    the drivers use only the caller's workspace.  Outputs must not alias
