@@ -202,8 +202,10 @@ __global__ __launch_bounds__(512) void partial_bf16_fast_kernel(const PartialLau
   float* const seg_lse = reinterpret_cast<float*>(qsm) + wave * 32 * 64;
 
   // normalise and store this lane's row of segment `seg` (slot item.slot + seg)
-  // from the running reference m_ and row share l_
-  auto write_out = [&](int seg, float m_, float l_) {
+  // from the running reference m_ and row share l_; with `keep` the row is not
+  // stored but left in o, its factor in keep_s, for the merge tail to take
+  float keep_s = 0.f;
+  auto write_out = [&](int seg, float m_, float l_, bool keep) {
     const float l_tot = pair32_sum(l_);
     if (row < a.Sq) {
       const bool acc = !SEG && a.accumulate != 0;  // chunk walks never accumulate
@@ -220,17 +222,20 @@ __global__ __launch_bounds__(512) void partial_bf16_fast_kernel(const PartialLau
         for (int k = 0; k < NP; ++k) old[k] = *reinterpret_cast<const f32x4*>(orow + (k >> 2) * 32 + 8 * (k & 3));
       }
       const RowOut ro = row_out(m_, l_tot, acc, lse_old);
+      keep_s = ro.s_new;
+      if (!keep) {
 #pragma unroll
-      for (int k = 0; k < NP; ++k) {
-        const int db = k >> 2, i4 = k & 3;
-        f32x4 v4 = {o[db][4 * i4 + 0] * ro.s_new, o[db][4 * i4 + 1] * ro.s_new, o[db][4 * i4 + 2] * ro.s_new,
-                    o[db][4 * i4 + 3] * ro.s_new};
-        if (acc)
-          v4 = (f32x4){fmaf(old[k][0], ro.s_old, v4[0]), fmaf(old[k][1], ro.s_old, v4[1]),
-                       fmaf(old[k][2], ro.s_old, v4[2]), fmaf(old[k][3], ro.s_old, v4[3])};
-        *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * i4) = v4;
+        for (int k = 0; k < NP; ++k) {
+          const int db = k >> 2, i4 = k & 3;
+          f32x4 v4 = {o[db][4 * i4 + 0] * ro.s_new, o[db][4 * i4 + 1] * ro.s_new, o[db][4 * i4 + 2] * ro.s_new,
+                      o[db][4 * i4 + 3] * ro.s_new};
+          if (acc)
+            v4 = (f32x4){fmaf(old[k][0], ro.s_old, v4[0]), fmaf(old[k][1], ro.s_old, v4[1]),
+                         fmaf(old[k][2], ro.s_old, v4[2]), fmaf(old[k][3], ro.s_old, v4[3])};
+          *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * i4) = v4;
+        }
+        if (g == 0 && lps != nullptr) lps[(int64_t)row * a.l_ss] = ro.lse;
       }
-      if (g == 0 && lps != nullptr) lps[(int64_t)row * a.l_ss] = ro.lse;
       if constexpr (SEG)
         if (g == 0 && a.final_out != nullptr) seg_lse[seg * 32 + l32] = ro.lse;
     }
@@ -435,7 +440,7 @@ __global__ __launch_bounds__(512) void partial_bf16_fast_kernel(const PartialLau
         if (do_fetch) fetch(SL);
         if constexpr (SEG) {
           if (pend) {
-            write_out(seg_pend, m_pend, l_pend);
+            write_out(seg_pend, m_pend, l_pend, false);
 #pragma unroll
             for (int db = 0; db < NDB; ++db) o[db] = (f32x16){};
             pend = false;
@@ -580,18 +585,38 @@ __global__ __launch_bounds__(512) void partial_bf16_fast_kernel(const PartialLau
   }
 
   const int last_seg = SEG && n_tiles > 0 ? (n_tiles - 1) / a.seg_tiles : 0;
-  write_out(last_seg, m, l);
+  // Both ring orders merge the owner's own chunk first.  When that chunk is also
+  // the last one this walk computed (every query tile of a causal prefill at
+  // equal lengths), its partial is still in o: the merge tail takes it from
+  // there instead of storing it and reading it back.
+  const bool keep_first = SEG && a.final_out != nullptr && last_seg == it.q_chunk;
+  write_out(last_seg, m, l, keep_first);
   if constexpr (SEG) {
     // Segments past this query tile's last visible key hold pairs its rows see
     // nothing of (queries shorter than K/V put the last chunk's first keys after
     // the early rows): each gets the empty partial, O = 0 and LSE = -inf.
     const int n_seg = (Sk + a.seg_tiles * BN - 1) / (a.seg_tiles * BN);
     if (last_seg + 1 < n_seg) {
+      if (keep_first) {
+        // o still holds the kept partial: store the empty ones directly (the
+        // bits write_out stores for a zeroed o and no key: +0 and -inf)
+        if (row < a.Sq) {
+          constexpr int NP = 4 * NDB;
+          for (int seg = last_seg + 1; seg < n_seg; ++seg) {
+            float* const orow = op + seg * a.o_slot + (int64_t)row * a.o_ss + 4 * g;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) o[db] = (f32x16){};
-      m = kNegInf;
-      l = 0.f;
-      for (int seg = last_seg + 1; seg < n_seg; ++seg) write_out(seg, m, l);
+            for (int k = 0; k < NP; ++k) *reinterpret_cast<f32x4*>(orow + (k >> 2) * 32 + 8 * (k & 3)) = (f32x4){};
+            if (g == 0 && lp != nullptr) lp[seg * a.l_slot + (int64_t)row * a.l_ss] = kNegInf;
+            if (g == 0) seg_lse[seg * 32 + l32] = kNegInf;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db] = (f32x16){};
+        m = kNegInf;
+        l = 0.f;
+        for (int seg = last_seg + 1; seg < n_seg; ++seg) write_out(seg, m, l, false);
+      }
     }
     if (a.final_out != nullptr && row < a.Sq) {
       // Merge tail: this lane's pieces of the n_seg partials it has just
@@ -616,7 +641,15 @@ __global__ __launch_bounds__(512) void partial_bf16_fast_kernel(const PartialLau
       if (M != kNegInf) {
         f32x4 cur[NP], nxt[NP];
         int j = arrival_kv(pq, i, n_seg, 0);
-        load_seg(j, cur);
+        if (keep_first) {
+          // the partial write_out would have stored: the same products of o and s_new
+#pragma unroll
+          for (int k = 0; k < NP; ++k)
+            cur[k] = (f32x4){o[k >> 2][4 * (k & 3) + 0] * keep_s, o[k >> 2][4 * (k & 3) + 1] * keep_s,
+                             o[k >> 2][4 * (k & 3) + 2] * keep_s, o[k >> 2][4 * (k & 3) + 3] * keep_s};
+        } else {
+          load_seg(j, cur);
+        }
         for (int c = 0; c < n_seg; ++c) {
           const int jn = c + 1 < n_seg ? arrival_kv(pq, i, n_seg, c + 1) : j;
           if (c + 1 < n_seg) load_seg(jn, nxt);

@@ -192,7 +192,10 @@ cpattn_status cpattn_ring_select_order(const cpattn_tensor* q, const cpattn_tens
  *   out [B, Sq, Hq, D] F32 or BF16
  *   lse [B, Sq, Hq]    F32, or NULL
  *   workspace          device buffer of at least
- *                      cpattn_ring_prefill_workspace_size(q, k, n_chunks, causal) bytes
+ *                      cpattn_ring_prefill_workspace_size(q, k, n_chunks, causal) bytes;
+ *                      scratch of this call (its contents afterwards are unspecified:
+ *                      the walk keeps a query tile's own-chunk partial in registers
+ *                      when it is the last one the tile computes)
  */
 cpattn_status cpattn_ring_prefill(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
                                   int n_chunks, int order /* cpattn_order */, int causal,
