@@ -42,7 +42,7 @@ def suffix_reference(q, k, v, causal):
 
 # (B, Sq, Skv, P, Hq, Hkv, D, dtype): bf16 with K/V chunks of a multiple of 64 keys (up to 16384)
 # takes the per-owner walk when the owners' query tiles number at least two per compute unit (the
-# last three cases, on 256 of them; two of those also pack heads), the others one work item per pair
+# last four cases, on 256 of them; two of those also pack heads), the others one work item per pair
 SUFFIX_CASES = [
     (1, 512, 2048, 4, 4, 1, 128, "bf16"),     # 512-key chunks, 128-query chunks
     (2, 300, 12480, 3, 4, 2, 128, "bf16"),    # 4160-key chunks, ragged 100-query chunks
@@ -55,6 +55,10 @@ SUFFIX_CASES = [
     (8, 512, 2048, 4, 16, 1, 128, "bf16"),    # walk, 128-query chunks, two heads to a workgroup
     (12, 300, 3840, 3, 16, 2, 128, "bf16"),   # walk, ragged 100-query chunks, 1280-key chunks
     (8, 64, 8192, 16, 8, 1, 128, "bf16"),     # walk, 4 queries per chunk, four heads to a workgroup
+    # walk with queries just shorter than K/V: the first query tiles of owners 0-2 end inside their
+    # own chunk (their partial stays in registers for the merge tail) yet store an empty partial
+    # for the next chunk, which the owner's later rows see
+    (2, 4032, 4096, 4, 16, 1, 128, "bf16"),
 ]
 
 
