@@ -620,7 +620,8 @@ __global__ __launch_bounds__(512) void partial_bf16_fast_kernel(const PartialLau
     }
     if (a.final_out != nullptr && row < a.Sq) {
       // Merge tail: this lane's pieces of the n_seg partials it has just
-      // written, in the ring order's arrival order, with the arithmetic of the
+      // written (the first in arrival order, the own chunk's, taken from o when
+      // kept), in the ring order's arrival order, with the arithmetic of the
       // ring merge kernel (the same pieces in the same order: bit-identical).
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
       const int i = it.q_chunk;
