@@ -237,8 +237,9 @@ def test_concurrent_streams_bit_identical(cp):
 def test_graph_capture_replays(cp):
     """The ring entry points and the allocation-free decode, given their buffers, issue only kernel
     launches on the caller's stream, so a caller can capture them in a HIP graph: the 4 accumulating
-    ring steps, a Pass-Q ring prefill, the fused prefill and a decode, captured once and replayed
-    three times with eager work between the replays, give the eager bits every time."""
+    ring steps, a Pass-Q ring prefill as per-pair launches and the merge, a Pass-KV ring prefill
+    sized for the chunk walk (512 walking workgroups), the fused prefill and a decode, captured once
+    and replayed three times with eager work between the replays, give the eager bits every time."""
     P = 4
     q, k, v = qkv(51, 4096, 8, 1, 128)
     qd = si.draw_tensor(52, 0, (8, 1, 16, 128), torch.bfloat16).to(DEV)
@@ -246,6 +247,9 @@ def test_graph_capture_replays(cp):
     vd = si.draw_tensor(52, 2, (8, 4096, 1, 128), torch.bfloat16).to(DEV)
     bufs = {name: (torch.empty(1, 4096, 8, 128, device=DEV), torch.empty(1, 4096, 8, device=DEV))
             for name in ("acc", "ring", "fused")}
+    qw, kw, vw = qkv(53, 4096, 8, 1, 128, B=4)
+    bufs["walk"] = (torch.empty(4, 4096, 8, 128, device=DEV), torch.empty(4, 4096, 8, device=DEV))
+    ws_w = torch.empty(cp.ring_prefill_workspace_size(qw, P, True), dtype=torch.uint8, device=DEV)
     dec = (torch.empty(8, 1, 16, 128, device=DEV), torch.empty(8, 1, 16, device=DEV))
     ws = torch.empty(cp.ring_prefill_workspace_size(q, P, True), dtype=torch.uint8, device=DEV)
 
@@ -253,6 +257,7 @@ def test_graph_capture_replays(cp):
         for step in range(P):
             cp.ring_step_accumulate(q, k, v, P, step, *bufs["acc"], "pass_kv", True)
         cp.ring_prefill(q, k, v, P, "pass_q", True, out=bufs["ring"][0], lse=bufs["ring"][1], workspace=ws)
+        cp.ring_prefill(qw, kw, vw, P, "pass_kv", True, out=bufs["walk"][0], lse=bufs["walk"][1], workspace=ws_w)
         cp.ring_prefill_fused(q, k, v, P, True, out=bufs["fused"][0], lse=bufs["fused"][1])
         cp.splitkv_decode_noalloc(qd, kd, vd, 8, *dec)
 
