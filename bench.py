@@ -48,7 +48,7 @@ DECODE_FILE = os.path.join(ROOT, "profiles", "decode_stream_b128_kv32k_p8.txt")
 DECODE_PROFILE_CMD = "python $R/bench.py --decode-only"
 MERGE_FILE = os.path.join(ROOT, "profiles", "ring_merge_s128k_p16.txt")
 MERGE_PROFILE_CMD = "python $R/bench.py --merge-only"
-PROFILE_CMD = "python bench.py --headline-only --no-cpu-baseline"
+PROFILE_CMD = "python $R/bench.py --headline-only --no-cpu-baseline"
 COPY_BYTES = 1 << 30
 
 
@@ -880,8 +880,8 @@ def summarize_trace(trace_dir: str, bench_json: str) -> int:
         f.write("# On the MI355X machine, from /tmp with TMPDIR=/tmp, R = repository root, OUT = an output directory:\n")
         f.write(f"#   rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/trace -o kt -- "
                 f"{PROFILE_CMD} --steps 5 --warmup 1\n")
-        f.write(f"#   python bench.py --summarize-trace $OUT/trace $OUT/bench_plain.json\n")
-        f.write("# where $OUT/bench_plain.json is the plain `python bench.py` line of the same run (same machine).\n")
+        f.write(f"#   python $R/bench.py --summarize-trace $OUT/trace $OUT/bench_plain.json\n")
+        f.write("# where $OUT/bench_plain.json is the plain `python $R/bench.py` line of the same call (same machine).\n")
         f.write(f"kernel_source_sha256_16: {kernel_hash()}\n")
         f.write(f"machine_host: {line['roofline'].get('machine', {}).get('host')}\n")
         f.write(f"machine_gpu_uuid: {line['roofline'].get('machine', {}).get('gpu_uuid')}\n")
@@ -891,8 +891,8 @@ def summarize_trace(trace_dir: str, bench_json: str) -> int:
         f.write(f"tflops_profiled: {tfl:.1f}\n")
         f.write(f"frac_profiled: {tfl / PEAK_BF16_TFLOPS:.4f}\n")
         f.write(f"trace_kernel_ms_per_step: {avg_ns * w.n_chunks / 1e6:.3f}\n")
-        f.write("# (the traced run has the profiler attached and runs after the plain bench; its launches\n"
-                "# read a little longer than the plain run's event timing)\n")
+        f.write("# (the traced run has the profiler attached and runs after the plain bench; the clock the\n"
+                "# chip holds moves between the runs, so its launches read a little longer or shorter)\n")
         f.write("# the plain bench line of the same call (HIP events around each launch; no profiler attached)\n")
         f.write(f"bench_ms_per_step: {line['ms_per_step']}\n")
         f.write(f"bench_value_tflops: {line['value']}\n")
